@@ -1,0 +1,211 @@
+"""Benchmark of the suffix-replay hot path on one MI355X.
+
+Default workload: the gated-delta-rule replay of one GDN layer for 16 hits of
+a 32K-token matched prefix with a 10 % replay budget (k = 3276 anchors each),
+16 key / 32 value heads, d = 128, bf16 inputs, chunk 64 -- the configuration
+the headline metric (replayed tokens/s per GDN layer and the fraction of the
+roofline) is quoted on.  A step is one replay of that batch through
+sr_gdn_replay_state (states + per-token outputs), inputs resident in HBM.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one
+GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2500.0  # dense fp16/bf16 matrix cores
+
+
+def gdn_algorithmic(n_seqs, seqlen, h_k, h_v, d, in_bytes=2, out_bytes=2, chunk=64,
+                    want_o=True, erase=True):
+    """Algorithmic bytes (each input read once, each output written once) and
+    nominal matrix-core FLOPs of the chunked algorithm for one launch."""
+    T = n_seqs * seqlen
+    byts = T * h_k * d * in_bytes                    # k
+    byts += T * h_v * d * in_bytes                   # v
+    byts += T * h_v * 4 * (2 if erase else 1)        # alpha (+ beta)
+    byts += n_seqs * h_v * d * d * 4                 # final state
+    if want_o:
+        byts += T * h_k * d * in_bytes               # q
+        byts += T * h_v * d * out_bytes              # o
+    C = chunk
+    if erase and want_o:
+        per = 10 * C * d + 6 * d * d + C * C / 3
+    elif erase:
+        per = 6 * C * d + 4 * d * d + C * C / 3
+    elif want_o:
+        per = 4 * C * d + 4 * d * d
+    else:
+        per = 2 * d * d
+    flops = T * h_v * per
+    return byts, flops
+
+
+def kernel_source_hash():
+    p = os.path.join(ROOT, "linear_attention_state_anchor_amd", "csrc", "gdn_chunk.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(bytes_alg):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "gdn_chunk_gdn16x3276_pmc.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s=20.0):
+    """Time the fp64 oracle (as it stands) on whole sequences of the same
+    workload, as many as fit about budget_s of host time."""
+    import numpy as np
+    import oracle
+    from replay_inputs import gdn_case
+
+    cu = case.cu_seqlens
+
+    def sub(seqs):
+        idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+        c = gdn_case([int(cu[s + 1] - cu[s]) for s in seqs], case.h_k, case.h_v, case.d_k,
+                     case.dtype, seed=0, erase=case.erase)
+        c.q, c.k, c.v, c.alpha = case.q[idx], case.k[idx], case.v[idx], case.alpha[idx]
+        c.beta = None if case.beta is None else case.beta[idx]
+        c.alpha_is_log = case.alpha_is_log
+        return c
+
+    def run(c):
+        t0 = time.perf_counter()
+        oracle.gdn(c.q, c.k, c.v, c.alpha, c.beta, c.cu_seqlens, c.h_k, c.h_v,
+                   alpha_is_log=c.alpha_is_log, erase=c.erase)
+        return time.perf_counter() - t0
+
+    threads = oracle.max_threads()
+    first = sub([0])
+    t1 = run(first)
+    n = int(max(1, min(case.n_seqs, budget_s // max(t1, 1e-3))))
+    seqs = list(range(n))
+    c = sub(seqs)
+    t = run(c)
+    toks = c.total_tokens
+    return {"value": toks / t, "unit": "replayed tokens/s per GDN layer", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {case.n_seqs} sequences ({toks} tokens, all {case.h_v} value "
+                      f"heads), fp64 token loop, {t:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the replay "
+              "path has no cross-GPU part in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import linear_attention_state_anchor_amd as sr
+    from replay_inputs import config_c3
+
+    def to_dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:  # bf16 bit patterns
+            return torch.from_numpy(x.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        return torch.from_numpy(x).to("cuda:0")
+
+    case = config_c3()
+    n, L, hk, hv, d = case.n_seqs, 3276, case.h_k, case.h_v, case.d_k
+    T = case.total_tokens
+    dev = torch.device("cuda:0")
+    q, k, v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+    alpha, beta, cu = to_dev(case.alpha), to_dev(case.beta), to_dev(case.cu_seqlens)
+    S = torch.empty((n, hv, d, d), dtype=torch.float32, device=dev)
+    o = torch.empty((T, hv, d), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        sr.gdn_replay_state(q, k, v, alpha, beta, cu, None, alpha_is_log=True,
+                            final_state=S, o=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    assert bool(torch.isfinite(S).all()), "non-finite state"
+
+    byts, flops = gdn_algorithmic(n, L, hk, hv, d)
+    sec = ms / 1e3
+    achieved = byts / sec / 1e9
+    traffic = read_traffic(byts)
+    line = {
+        "metric": "replayed tokens/s per GDN layer (+ % of MI355X HBM / bf16-fp16 MFMA "
+                  "roofline), 32K prefix, 10% suffix",
+        "value": T / sec,
+        "unit": "replayed tokens/s per GDN layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gated-delta-rule replay, 16 hits x 3276 anchors (10% of a 32K "
+                        "prefix), 16 key / 32 value heads, d=128, chunk 64, bf16 in/out, "
+                        "fp32 state",
+            "n_seqs": n, "suffix": L, "h_k": hk, "h_v": hv, "d": d, "chunk": 64,
+            "kernel": "gdn_chunk_kernel (fp16 MFMA operands, fp32 accumulate)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "mfma": {
+            "achieved_tflops": flops / sec / 1e12,
+            "peak_tflops": MFMA_F16_PEAK_TFS,
+            "frac": flops / sec / 1e12 / MFMA_F16_PEAK_TFS,
+            "flop_per_launch": flops,
+            "bytes_per_launch": byts,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,26 +4,31 @@
 // erase; "Tail-Replay", section 2)
 //     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t
 // is evaluated 64 tokens at a time.  Within a chunk (g_t = log a_t,
-// G_t = sum_{s<=t} g_s, everything below is exact algebra of the recurrence):
-//     A[t][j] = b_t e^{G_t-G_j} (k_t . k_j), j < t        (strictly lower)
-//     Tm      = (I + A)^{-1}
-//     W       = Tm diag(b e^G) K,   U~ = Tm diag(b) V
-//     U       = U~ - W S^T                                  (needs the carry)
-//     O       = diag(e^G) Q S^T + (P o Q K^T) U,  P[t][j] = e^{G_t-G_j}, j<=t
-//     S^T    <- e^{G_C} S^T + K^T diag(e^{G_C-G}) U
+// G_t = sum_{s<=t} g_s; exact algebra of the recurrence):
+//     A[t][j] = b_t e^{G_t-G_j} (k_t . k_j), j < t          (strictly lower)
+//     (I + A) [W | U~] = [diag(b e^G) K | diag(b) V]
+//     U  = U~ - W S^T                                         (needs the carry)
+//     O  = diag(e^G) Q S^T + (P o Q K^T) U,   P[t][j] = e^{G_t-G_j}, j <= t
+//     S^T <- e^{G_C} S^T + K^T diag(e^{G_C-G}) U
 // Erase-free mode (scalar decay only): A = 0, U = diag(b) V.
 //
-// Layout of the work: one workgroup (4 waves) per (sequence, value head)
-// walks that sequence's chunks in order.  The transposed state S^T (d_k x
-// d_v, fp32) stays in matrix-core accumulator registers for the whole
-// sequence; wave w owns value columns [w*D/4, (w+1)*D/4).  Accumulator tiles
-// of S^T, U and O feed the next products directly as B operands: two
-// vertically adjacent 16x16 accumulator tiles hold, per lane, the 8 k-slots
-// {4g..4g+3, 16+4g..16+4g+3} (g = lane/16) of a K = 32 operand, and the A
-// operand is read from LDS in the same k order.  Operands are fp16 (bf16
-// inputs convert exactly); accumulation and the state are fp32.
-// The 64x64 triangular inverse is done in fp32 in LDS by blocked forward
-// substitution (16x16 diagonal blocks, then block columns).
+// The triangular system is solved by block forward substitution over 16-row
+// blocks: the four 16x16 diagonal blocks are inverted in fp32 (one wave
+// each), then block row i of [W | U~] is (I + A_ii)^{-1} (R_i - sum_{m<i}
+// A_im Y_m), all on the matrix cores with register-resident operands.
+//
+// Work layout: one workgroup (4 waves) per (sequence, value head) walks the
+// sequence's chunks in order; wave w owns value columns and key columns
+// [w*D/4, (w+1)*D/4).  The transposed state S^T (d_k x d_v, fp32) stays in
+// accumulator registers for the whole sequence.  Accumulator tiles feed later
+// products directly as operands: two vertically adjacent 16x16 tiles hold,
+// per lane, the k-slots {4g..4g+3, 16+4g..16+4g+3} (g = lane/16) of a K = 32
+// operand, and the other operand is read from LDS in the same k order.
+// Operands are fp16 (bf16 inputs convert exactly); accumulation and the
+// state are fp32.  The next chunk's K, Q and V are prefetched into registers
+// while the current chunk computes, so each chunk has a single staging
+// barrier.  Workgroups are numbered so that the value heads sharing a key
+// head run on the same XCD (shared L2 for their K and Q).
 #include "sr_common.hpp"
 #include "sr_internal.hpp"
 
@@ -31,28 +36,22 @@ namespace sr {
 
 namespace {
 
-constexpr int kC = 64;          // chunk length (tokens)
-constexpr int kThreads = 256;   // 4 waves
-constexpr int kTS = kC + 8;     // fp16 row stride of [.][64] LDS tiles
-constexpr int kAS = kC + 4;     // fp32 row stride of the 64x64 fp32 tiles
+constexpr int kC = 64;         // chunk length (tokens)
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kAS = kC + 4;    // fp32 row stride of A
+constexpr int kPS = kC + 4;    // fp16 row stride of P o QK^T
+constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
 
 template <int D>
 struct ChunkSmem {
-  static constexpr int kWS = D + 8;  // fp16 row stride of the [64][D] W tile
-  _Float16 kt[D * kTS];              // K^T of the chunk  [j][t]
-  _Float16 vt[D * kTS];              // V^T of the chunk  [i][t]
-  union {
-    float a[kC * kAS];               // A (fp32)          [t][j]
-    _Float16 w[kC * kWS];            // -W                [t][j]
-  } aw;
-  union {
-    float tm[kC * kAS];              // (I+A)^-1 (fp32) while solving
-    struct {
-      _Float16 tb[kC * kTS];         // Tm diag(b)
-      _Float16 tbg[kC * kTS];        // Tm diag(b e^G)
-    } t16;
-    _Float16 pqk[kC * kTS];          // P o (Q K^T)
-  } tt;
+  static constexpr int kWS = D + 4;  // fp16 row stride of -W
+  static constexpr int kKS = D + 8;  // fp16 row stride of the K and Q rows
+  _Float16 k[kC * kKS];              // K rows
+  _Float16 q[kC * kKS];              // Q rows
+  float a[kC * kAS];                 // A, fp32 (strictly lower blocks)
+  _Float16 w[kC * kWS];              // -W
+  _Float16 pqk[kC * kPS];            // P o (Q K^T)
+  _Float16 td[4 * 16 * 16];          // (I + A_bb)^{-1}, row-major per block
   float gcum[kC];                    // G_t
   float gam[kC];                     // e^{G_t}
   float dec[kC];                     // e^{G_C - G_t}
@@ -60,49 +59,76 @@ struct ChunkSmem {
   float bg[kC];                      // b_t e^{G_t}
 };
 
-// 16x16 tile MFMA over K = 32 with both operands 8 consecutive fp16 in LDS.
+// element (t, j) of a padded [64][D] fp16 row tile (rows 16-byte aligned,
+// consecutive rows 4 banks apart)
+template <int D>
+__device__ __forceinline__ int swz(int t, int j) {
+  return t * (D + 8) + j;
+}
+
 __device__ __forceinline__ f16x8 lds8(const _Float16* p) {
   return *reinterpret_cast<const f16x8*>(p);
 }
 __device__ __forceinline__ f16x4 lds4(const _Float16* p) {
   return *reinterpret_cast<const f16x4*>(p);
 }
-// A operand in the permuted k order {4g..4g+3, 16+4g..16+4g+3} of a 32-wide
-// k block starting at p (p already offset by the row).
-__device__ __forceinline__ f16x8 lds_perm(const _Float16* p, int lg) {
-  return cat44(lds4(p + 4 * lg), lds4(p + 16 + 4 * lg));
+
+__device__ __forceinline__ f32x4 mfma16x16x16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Keeps the scheduler from hoisting the loads of later unrolled iterations
+// above this point (which would make their registers live all at once).
+#define SR_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+__device__ __forceinline__ f16x4 neg_f16x4(f32x4 v) {
+  return to_f16x4(-v);
+}
+
+template <typename TI>
+__device__ __forceinline__ _Float16 raw_to_f16(uint16_t b);
+template <>
+__device__ __forceinline__ _Float16 raw_to_f16<BF16>(uint16_t b) {
+  return static_cast<_Float16>(bf16_to_f32(b));
+}
+template <>
+__device__ __forceinline__ _Float16 raw_to_f16<F16>(uint16_t b) {
+  return __builtin_bit_cast(_Float16, b);
 }
 
 template <int D, typename TI, typename TO, bool ERASE>
-__global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a) {
-  constexpr int IW = D / 4;       // value columns per wave
-  constexpr int NIT = IW / 16;    // 16-wide value tiles per wave
+__global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
+  constexpr int IW = D / 4;       // value (and key) columns per wave
+  constexpr int NIT = IW / 16;    // 16-wide column tiles per wave
   constexpr int NJT = D / 16;     // 16-wide key tiles
   constexpr int NKJ = D / 32;     // K = 32 steps over the key dimension
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int NPF = CPR / 4;    // 16-byte K (and Q) row pieces per thread
   constexpr int kWS = ChunkSmem<D>::kWS;
   static_assert(NIT >= 1, "D too small");
 
   __shared__ ChunkSmem<D> sm;
 
-  const int n = blockIdx.x / a.h_v;
-  const int h = blockIdx.x % a.h_v;
+  // XCD-aware numbering: consecutive (sequence, head) units share an XCD.
+  const int unit = (blockIdx.x % kXcd) * units_per_xcd + blockIdx.x / kXcd;
+  if (unit >= a.n_seqs * a.h_v) return;  // padding workgroup
+  const int n = unit / a.h_v;
+  const int h = unit % a.h_v;
   const int g = h / (a.h_v / a.h_k);
   const int tid = threadIdx.x;
-  const int w = tid / kWave;
-  const int l = tid % kWave;
-  const int lr = l % 16;
-  const int lg = l / 16;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const bool want_o = a.o != nullptr;
-  const size_t qk_stride = static_cast<size_t>(a.h_k) * D;   // per token
-  const size_t v_stride = static_cast<size_t>(a.h_v) * D;
-  const char* qg = static_cast<const char*>(a.q) + static_cast<size_t>(g) * D * Ld8<TI>::kBytes;
-  const char* kg = static_cast<const char*>(a.k) + static_cast<size_t>(g) * D * Ld8<TI>::kBytes;
-  const char* vg = static_cast<const char*>(a.v) + static_cast<size_t>(h) * D * Ld8<TI>::kBytes;
-  constexpr int EB = Ld8<TI>::kBytes;
+  const size_t qk_row = static_cast<size_t>(a.h_k) * D;  // elements per token
+  const size_t v_row = static_cast<size_t>(a.h_v) * D;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(g) * D;
+  const uint16_t* qg = want_o ? static_cast<const uint16_t*>(a.q) + static_cast<size_t>(g) * D
+                              : nullptr;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(h) * D;
 
-  // S^T accumulators: tile (jt, it) covers key rows 16jt.., value columns
+  // S^T accumulators: tile (jt, it) = key rows 16jt.., value columns
   // w*IW + 16it..; lane holds column lr, rows 4lg..4lg+3.
   f32x4 S[NJT][NIT];
+  int lr = tid % 16, lg = (tid / 16) % 4, l = tid % kWave;
   const size_t sbase = (static_cast<size_t>(n) * a.h_v + h) * D * D;
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt)
@@ -115,44 +141,104 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a) {
         S[jt][it][r] = a.s0 ? a.s0[sbase + static_cast<size_t>(j) * D + i] : 0.0f;
       }
 
+  // P o QK^T tiles (0,1) and (2,3) are read as zeros by the K = 32 steps of
+  // the output product and never written otherwise
+  for (int e = tid; e < 256; e += kThreads) {
+    const int rr = e / 16, cc = e % 16;
+    sm.pqk[rr * kPS + 16 + cc] = static_cast<_Float16>(0.0f);
+    sm.pqk[(32 + rr) * kPS + 48 + cc] = static_cast<_Float16>(0.0f);
+  }
+
   const int t_begin = a.cu[n];
   const int t_end = a.cu[n + 1];
 
-  for (int c0 = t_begin; c0 < t_end; c0 += kC) {
-    const int nv = min(kC, t_end - c0);
-
-    // ---- stage K^T, V^T (fp16) and the gate scalars ----------------------
-    for (int item = tid; item < (kC / 2) * (D / 8); item += kThreads) {
-      const int p = item / (D / 8);
-      const int jc = item % (D / 8);
-      const int t = 2 * p;
-      f16x8 r0 = {}, r1 = {};
-      if (t < nv) r0 = Ld8<TI>::load(kg + ((c0 + t) * qk_stride + 8 * jc) * EB);
-      if (t + 1 < nv) r1 = Ld8<TI>::load(kg + ((c0 + t + 1) * qk_stride + 8 * jc) * EB);
+  // ---- prefetch registers (raw input bits) for the next chunk -------------
+  // Addresses are a uniform row base (scalar registers) plus a per-lane
+  // offset that does not change between chunks.
+  u16x8 pk[NPF], pq[NPF];
+  u16x4 pv[4][NIT];      // V in accumulator layout: rows 16bi+4lg+r, column lr
+  float pa = 0.0f, pb = 0.0f;
+  auto kq_lane = [&]() { return ((w * kWave + l) / CPR) * static_cast<int>(qk_row) + 8 * ((w * kWave + l) % CPR); };
+  auto v_lane = [&]() { return 4 * lg * static_cast<int>(v_row) + w * IW + lr; };
+  auto prefetch_kq = [&](int c0n) {
+    const int nvn = min(kC, t_end - c0n);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        f16x2 pr = {r0[e], r1[e]};
-        *reinterpret_cast<f16x2*>(&sm.kt[(8 * jc + e) * kTS + t]) = pr;
-      }
-      f16x8 v0 = {}, v1 = {};
-      if (t < nv) v0 = Ld8<TI>::load(vg + ((c0 + t) * v_stride + 8 * jc) * EB);
-      if (t + 1 < nv) v1 = Ld8<TI>::load(vg + ((c0 + t + 1) * v_stride + 8 * jc) * EB);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        f16x2 pr = {v0[e], v1[e]};
-        *reinterpret_cast<f16x2*>(&sm.vt[(8 * jc + e) * kTS + t]) = pr;
+    for (int e = 0; e < NPF; ++e) {
+      const int row = (w * kWave + l) / CPR + (kThreads / CPR) * e;
+      const uint16_t* kb = kg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
+      pk[e] = u16x8{};
+      pq[e] = u16x8{};
+      if (row < nvn) {
+        pk[e] = *reinterpret_cast<const u16x8*>(kb + kq_lane());
+        if (want_o) {
+          const uint16_t* qb = qg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
+          pq[e] = *reinterpret_cast<const u16x8*>(qb + kq_lane());
+        }
       }
     }
     if (w == 0) {
-      const bool ok = l < nv;
-      const size_t gi = static_cast<size_t>(c0 + l) * a.h_v + h;
-      float gl = 0.0f, be = 0.0f;
-      if (ok) {
-        const float al = a.alpha[gi];
-        gl = a.alpha_is_log ? al : __logf(al);
-        gl = fmaxf(gl, -64.0f);
-        be = a.beta ? a.beta[gi] : 1.0f;
+      pa = 0.0f;
+      pb = 0.0f;
+      if (l < nvn) {
+        const size_t gi = static_cast<size_t>(c0n + l) * a.h_v + h;
+        pa = a.alpha[gi];
+        pb = a.beta ? a.beta[gi] : 1.0f;
       }
+    }
+  };
+  auto prefetch_v = [&](int c0n) {
+    const int nvn = min(kC, t_end - c0n);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint16_t* vb = vg + static_cast<size_t>(c0n + 16 * bi + r) * v_row;
+        const bool ok = 16 * bi + 4 * lg + r < nvn;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) pv[bi][it][r] = ok ? vb[v_lane() + 16 * it] : uint16_t(0);
+      }
+  };
+  if (t_begin < t_end) {
+    prefetch_kq(t_begin);
+    prefetch_v(t_begin);
+  }
+
+  for (int c0 = t_begin; c0 < t_end; c0 += kC) {
+    const int nv = min(kC, t_end - c0);
+    // Re-derive the lane coordinates each chunk through an opaque copy so
+    // that the many lane-dependent LDS/global addresses are recomputed in the
+    // loop instead of being hoisted out of it (which would pin one register
+    // per address for the whole sequence).
+    {
+      int t_ = tid;
+      asm volatile("" : "+v"(t_));
+      l = t_ % kWave;
+      lr = t_ % 16;
+      lg = (t_ / 16) % 4;
+    }
+
+    // ---- stage this chunk: K, Q rows to LDS; gate scalars ----------------
+#pragma unroll
+    for (int e = 0; e < NPF; ++e) {
+      const int item = w * kWave + l + kThreads * e;
+      const int row = item / CPR, ch = item % CPR;
+      f16x8 kv, qv;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        kv[x] = raw_to_f16<TI>(pk[e][x]);
+        qv[x] = raw_to_f16<TI>(pq[e][x]);
+      }
+      const int dst = swz<D>(row, 8 * ch);
+      *reinterpret_cast<f16x8*>(&sm.k[dst]) = kv;
+      if (want_o) *reinterpret_cast<f16x8*>(&sm.q[dst]) = qv;
+    }
+    if (w == 0) {
+      float gl = 0.0f;
+      if (l < nv) {
+        gl = a.alpha_is_log ? pa : __logf(pa);
+        gl = fmaxf(gl, -64.0f);
+      }
+      const float be = l < nv ? pb : 0.0f;
       // inclusive prefix sum of the log-decays over the 64 lanes
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
@@ -169,285 +255,247 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a) {
     }
     __syncthreads();
 
-    // ---- A = strict lower part of b_t e^{G_t-G_j} K K^T (fp32) ------------
-    if (ERASE) {
-      for (int job = w; job < 10; job += 4) {
-        // lower-triangular 16x16 tiles in row-major order
-        const int tr = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
-        const int tc = job - tr * (tr + 1) / 2;
-        const int ta = 16 * tr + lr, tb_ = 16 * tc + lr;
+    // the next chunk's K, Q and gates fly while this one computes
+    const bool more = c0 + kC < t_end;
+    if (more) prefetch_kq(c0 + kC);
+
+    // ---- A (erase) and P o QK^T: lower-triangular 16x16 tiles -------------
+    {
+      const int njobs = (ERASE ? 10 : 0) + (want_o ? 10 : 0);
+      for (int job = w; job < njobs; job += 4) {
+        const bool is_kk = ERASE && job < 10;
+        const int tj = job % 10;
+        const int tr = tj < 1 ? 0 : tj < 3 ? 1 : tj < 6 ? 2 : 3;
+        const int tc = tj - tr * (tr + 1) / 2;
+        const _Float16* xa = is_kk ? sm.k : sm.q;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKJ; ++ks) {
-          f16x8 av = {}, bv = {};
-          if (ta < nv) av = Ld8<TI>::load(kg + ((c0 + ta) * qk_stride + 32 * ks + 8 * lg) * EB);
-          if (tb_ < nv) bv = Ld8<TI>::load(kg + ((c0 + tb_) * qk_stride + 32 * ks + 8 * lg) * EB);
+          const f16x8 av = lds8(&xa[swz<D>(16 * tr + lr, 32 * ks + 8 * lg)]);
+          const f16x8 bv = lds8(&sm.k[swz<D>(16 * tc + lr, 32 * ks + 8 * lg)]);
           acc = mfma16x16x32(av, bv, acc);
         }
         const int col = 16 * tc + lr;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * tr + 4 * lg + r;
-          float val = 0.0f;
-          if (row > col)
-            val = sm.beta[row] * __expf(sm.gcum[row] - sm.gcum[col]) * acc[r];
-          sm.aw.a[row * kAS + col] = val;
+          const float dgam = __expf(sm.gcum[row] - sm.gcum[col]);
+          if (is_kk)
+            sm.a[row * kAS + col] = row > col ? sm.beta[row] * dgam * acc[r] : 0.0f;
+          else
+            sm.pqk[row * kPS + col] = static_cast<_Float16>(row >= col ? dgam * acc[r] : 0.0f);
         }
       }
-      __syncthreads();
+    }
+    __syncthreads();
 
-      // ---- (I + A)^{-1}: 16x16 diagonal blocks by forward substitution --
-      if (w == 0) {
-        const int b = l / 16, c = l % 16;
+    // U accumulators: tile (tt, it) = token rows 16tt.., value columns
+    // w*IW + 16it..
+    f32x4 U[4][NIT];
+    if (ERASE) {
+      // ---- (I + A_bb)^{-1} for diagonal block b = w, fp32 ----------------
+      {
+        const int c = lr;
+        const float* ab = &sm.a[(16 * w) * kAS + 16 * w];
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float acc = (r == c) ? 1.0f : 0.0f;
-          const float* arow = &sm.aw.a[(16 * b + r) * kAS + 16 * b];
 #pragma unroll
-          for (int m = 0; m < r; ++m) acc = fmaf(-arow[m], x[m], acc);
+          for (int m = 0; m < r; ++m) acc = fmaf(-ab[r * kAS + m], x[m], acc);
           x[r] = acc;
         }
+        if (lg == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.tt.tm[(16 * b + r) * kAS + 16 * b + c] = x[r];
-      }
-      __syncthreads();
-      // ---- off-diagonal blocks, one block column per wave ---------------
-      // T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj
-#pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        const int jb = w;
-        const int ib = w + 1 + s;
-        const bool act = ib <= 3;
-        const int r = l / 4, c4 = 4 * (l % 4);
-        if (act) {
-          f32x4 x4 = {0.f, 0.f, 0.f, 0.f};
-          for (int m = jb; m < ib; ++m) {
-            const float* arow = &sm.aw.a[(16 * ib + r) * kAS + 16 * m];
-#pragma unroll
-            for (int mm = 0; mm < 16; ++mm) {
-              const f32x4 tv = *reinterpret_cast<const f32x4*>(
-                  &sm.tt.tm[(16 * m + mm) * kAS + 16 * jb + c4]);
-              x4 += arow[mm] * tv;
-            }
-          }
-          *reinterpret_cast<f32x4*>(&sm.tt.tm[(16 * ib + r) * kAS + 16 * jb + c4]) = x4;
-        }
-        __syncthreads();
-        if (act) {
-          f32x4 y4 = {0.f, 0.f, 0.f, 0.f};
-          const float* trow = &sm.tt.tm[(16 * ib + r) * kAS + 16 * ib];
-#pragma unroll
-          for (int mm = 0; mm < 16; ++mm) {
-            const f32x4 xv = *reinterpret_cast<const f32x4*>(
-                &sm.tt.tm[(16 * ib + mm) * kAS + 16 * jb + c4]);
-            y4 += trow[mm] * xv;
-          }
-          *reinterpret_cast<f32x4*>(&sm.tt.tm[(16 * ib + r) * kAS + 16 * jb + c4]) = -y4;
-        }
-        __syncthreads();
-      }
-      // ---- Tm diag(b) and Tm diag(b e^G) as fp16 ------------------------
-      {
-        float tv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int idx = tid + kThreads * e;
-          const int row = idx / kC, col = idx % kC;
-          tv[e] = col <= row ? sm.tt.tm[row * kAS + col] : 0.0f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int idx = tid + kThreads * e;
-          const int row = idx / kC, col = idx % kC;
-          sm.tt.t16.tb[row * kTS + col] = static_cast<_Float16>(tv[e] * sm.beta[col]);
-          sm.tt.t16.tbg[row * kTS + col] = static_cast<_Float16>(tv[e] * sm.bg[col]);
+          for (int r = 0; r < 16; ++r)
+            sm.td[w * 256 + r * 16 + c] = static_cast<_Float16>(x[r]);
         }
       }
       __syncthreads();
-    }
 
-    // ---- U~ (erase) or U (erase-free) for this wave's value columns -------
-    f32x4 U[4][NIT];
-    if (ERASE) {
+      // ---- block forward substitution for [W | U~], this wave's columns --
+      // column tile ct < NIT: W columns w*IW + 16ct (kept as -W in LDS);
+      // ct >= NIT: U~ columns w*IW + 16(ct-NIT) (kept in U).  Earlier block
+      // rows come back as fp16 B operands: W from LDS, U~ from registers.
+      auto yprev = [&](int m, int ct) -> f16x4 {
+        if (ct < NIT) {
+          const int j = w * IW + 16 * ct + lr;
+          f16x4 y;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          const int i = w * IW + 16 * it + lr;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            if (32 * ks > 16 * tt + 15) continue;  // Tm is lower triangular
-            const f16x8 av = lds8(&sm.tt.t16.tb[(16 * tt + lr) * kTS + 32 * ks + 8 * lg]);
-            const f16x8 bv = lds8(&sm.vt[i * kTS + 32 * ks + 8 * lg]);
-            acc = mfma16x16x32(av, bv, acc);
-          }
-          U[tt][it] = acc;
+          for (int r = 0; r < 4; ++r) y[r] = -sm.w[(16 * m + 4 * lg + r) * kWS + j];
+          return y;
         }
-      // -W^T = -(K^T (Tm diag(b e^G))^T) for this wave's key columns, to LDS
-      // as -W [t][j]
+        return to_f16x4(U[m][ct - NIT]);
+      };
 #pragma unroll
-      for (int jt = 0; jt < NIT; ++jt)
+      for (int bi = 0; bi < 4; ++bi) {
+        SR_SCHED_FENCE();
+        f32x4 X[2 * NIT];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          const int j = w * IW + 16 * jt + lr;
+        for (int ct = 0; ct < NIT; ++ct) {
+          const int j = w * IW + 16 * ct + lr;
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            if (32 * ks > 16 * tt + 15) continue;
-            const f16x8 av = lds8(&sm.kt[j * kTS + 32 * ks + 8 * lg]);
-            const f16x8 bv = lds8(&sm.tt.t16.tbg[(16 * tt + lr) * kTS + 32 * ks + 8 * lg]);
-            acc = mfma16x16x32(av, bv, acc);
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * bi + 4 * lg + r;
+            X[ct][r] = static_cast<float>(sm.k[swz<D>(t, j)]) * sm.bg[t];
+            X[NIT + ct][r] = static_cast<float>(raw_to_f16<TI>(pv[bi][ct][r])) * sm.beta[t];
           }
-          // acc: column t = 16tt + lr, rows j = w*IW + 16jt + 4lg + r
-          const int t = 16 * tt + lr;
-          *reinterpret_cast<f16x4*>(&sm.aw.w[t * kWS + w * IW + 16 * jt + 4 * lg]) =
-              to_f16x4(-acc);
         }
+        const float* arow = &sm.a[(16 * bi + lr) * kAS];
+        if (bi == 1) {
+          const f16x4 a4 = neg_f16x4(*reinterpret_cast<const f32x4*>(arow + 4 * lg));
+#pragma unroll
+          for (int ct = 0; ct < 2 * NIT; ++ct) X[ct] = mfma16x16x16(a4, yprev(0, ct), X[ct]);
+        } else if (bi >= 2) {
+          const f16x8 a8 = cat44(neg_f16x4(*reinterpret_cast<const f32x4*>(arow + 4 * lg)),
+                                 neg_f16x4(*reinterpret_cast<const f32x4*>(arow + 16 + 4 * lg)));
+#pragma unroll
+          for (int ct = 0; ct < 2 * NIT; ++ct)
+            X[ct] = mfma16x16x32(a8, cat44(yprev(0, ct), yprev(1, ct)), X[ct]);
+          if (bi == 3) {
+            const f16x4 a4 = neg_f16x4(*reinterpret_cast<const f32x4*>(arow + 32 + 4 * lg));
+#pragma unroll
+            for (int ct = 0; ct < 2 * NIT; ++ct) X[ct] = mfma16x16x16(a4, yprev(2, ct), X[ct]);
+          }
+        }
+        const f16x4 t4 = lds4(&sm.td[bi * 256 + lr * 16 + 4 * lg]);
+#pragma unroll
+        for (int ct = 0; ct < 2 * NIT; ++ct) {
+          const f32x4 y = mfma16x16x16(t4, to_f16x4(X[ct]), f32x4{0.f, 0.f, 0.f, 0.f});
+          if (ct < NIT) {
+            const int j = w * IW + 16 * ct + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              sm.w[(16 * bi + 4 * lg + r) * kWS + j] = static_cast<_Float16>(-y[r]);
+          } else {
+            U[bi][ct - NIT] = y;
+          }
+        }
+      }
+      __syncthreads();  // -W complete
     } else {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int i = w * IW + 16 * it + lr;
-          const f16x4 vv = lds4(&sm.vt[i * kTS + 16 * tt + 4 * lg]);
+        for (int it = 0; it < NIT; ++it)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            U[tt][it][r] = static_cast<float>(vv[r]) * sm.beta[16 * tt + 4 * lg + r];
-        }
+            U[tt][it][r] =
+                static_cast<float>(raw_to_f16<TI>(pv[tt][it][r])) * sm.beta[16 * tt + 4 * lg + r];
     }
 
-    __syncthreads();  // -W complete; Tm tiles dead
-
-    // ---- P o (Q K^T) into LDS (only the tiles the output product reads) ---
-    if (want_o) {
-      for (int job = w; job < 10; job += 4) {
-        const int tr = job < 1 ? 0 : job < 3 ? 1 : job < 6 ? 2 : 3;
-        const int tc = job - tr * (tr + 1) / 2;
-        const int ta = 16 * tr + lr, tb_ = 16 * tc + lr;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKJ; ++ks) {
-          f16x8 av = {}, bv = {};
-          if (ta < nv) av = Ld8<TI>::load(qg + ((c0 + ta) * qk_stride + 32 * ks + 8 * lg) * EB);
-          if (tb_ < nv) bv = Ld8<TI>::load(kg + ((c0 + tb_) * qk_stride + 32 * ks + 8 * lg) * EB);
-          acc = mfma16x16x32(av, bv, acc);
-        }
-        const int col = 16 * tc + lr;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * tr + 4 * lg + r;
-          float val = 0.0f;
-          if (row >= col) val = __expf(sm.gcum[row] - sm.gcum[col]) * acc[r];
-          sm.tt.pqk[row * kTS + col] = static_cast<_Float16>(val);
-        }
-      }
-      // upper tiles (0,1) and (2,3) are read by the K = 32 steps below
-      if (w == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = l + kWave * e;  // 0..255 over a 16x16 tile
-          const int rr = idx / 16, cc = idx % 16;
-          sm.tt.pqk[rr * kTS + 16 + cc] = static_cast<_Float16>(0.0f);
-          sm.tt.pqk[(32 + rr) * kTS + 48 + cc] = static_cast<_Float16>(0.0f);
-        }
-      }
-    }
-
-    // ---- U = U~ - W S^T and O = Q S^T, one key k-step at a time ----------
+    // ---- U = U~ - W S^T, one key k-step at a time -------------------------
     // S^T tiles 2kk and 2kk+1 form the fp16 B operand of k-step kk.
-    f32x4 O[4][NIT];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) O[tt][it] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (ERASE || want_o) {
+    if (ERASE) {
 #pragma unroll
       for (int kk = 0; kk < NKJ; ++kk) {
+        SR_SCHED_FENCE();
         f16x8 s16[NIT];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) s16[it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          const int t = 16 * tt + lr;
-          if (ERASE) {
-            const f16x8 av = lds_perm(&sm.aw.w[t * kWS + 32 * kk], lg);
+          const _Float16* wr = &sm.w[(16 * tt + lr) * kWS + 32 * kk];
+          const f16x8 av = cat44(lds4(wr + 4 * lg), lds4(wr + 16 + 4 * lg));
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(av, s16[it], U[tt][it]);
+          for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(av, s16[it], U[tt][it]);
+        }
+      }
+    }
+    // U as fp16 B operands: plain (output) and scaled by e^{G_C-G} (state)
+    f16x8 U16[2][NIT], UD[2][NIT];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        f32x4 lo = U[2 * ks][it], hi = U[2 * ks + 1][it];
+        if (want_o) U16[ks][it] = to_f16x8(lo, hi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          lo[r] *= sm.dec[32 * ks + 4 * lg + r];
+          hi[r] *= sm.dec[32 * ks + 16 + 4 * lg + r];
+        }
+        UD[ks][it] = to_f16x8(lo, hi);
+        // materialise the fp16 copies here so the fp32 U dies now instead of
+        // staying live through the output product
+        asm volatile("" : "+v"(UD[ks][it]));
+        if (want_o) asm volatile("" : "+v"(U16[ks][it]));
+      }
+
+    // ---- O = diag(e^G) Q S^T + (P o Q K^T) U, two token tiles at a time ----
+    if (want_o) {
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        f32x4 O[2][NIT];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) O[u][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKJ; ++kk) {
+          SR_SCHED_FENCE();
+          f16x8 s16[NIT];
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) s16[it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int t = 16 * (2 * tp + u) + lr;
+            const f16x8 qa = cat44(lds4(&sm.q[swz<D>(t, 32 * kk + 4 * lg)]),
+                                   lds4(&sm.q[swz<D>(t, 32 * kk + 16 + 4 * lg)]));
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(qa, s16[it], O[u][it]);
           }
-          if (want_o) {
-            f16x8 qa = {};
-            if (t < nv) {
-              const char* qrow = qg + ((c0 + t) * qk_stride + 32 * kk) * EB;
-              qa = cat44(ld4_f16<TI>(qrow + 4 * lg * EB), ld4_f16<TI>(qrow + (16 + 4 * lg) * EB));
-            }
+        }
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) O[tt][it] = mfma16x16x32(qa, s16[it], O[tt][it]);
+        for (int u = 0; u < 2; ++u) {
+          SR_SCHED_FENCE();
+          const int tt = 2 * tp + u;
+          const int t = 16 * tt + lr;
+#pragma unroll
+          for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[u][it][r] *= sm.gam[16 * tt + 4 * lg + r];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            if (32 * ks > 16 * tt + 15) continue;  // P o QK^T is lower triangular
+            const _Float16* pr = &sm.pqk[t * kPS + 32 * ks];
+            const f16x8 av = cat44(lds4(pr + 4 * lg), lds4(pr + 16 + 4 * lg));
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(av, U16[ks][it], O[u][it]);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const size_t ob = (static_cast<size_t>(c0 + 16 * tt + r) * a.h_v + h) * D;
+            if (16 * tt + 4 * lg + r < nv) {
+#pragma unroll
+              for (int it = 0; it < NIT; ++it)
+                store1<TO>(a.o, ob + v_lane() + 16 * it, a.scale * O[u][it][r]);
+            }
           }
         }
       }
     }
 
-    if (want_o) {
-      __syncthreads();  // P o QK^T complete
-      // O = diag(e^G) Q S^T + (P o Q K^T) U
-      f16x8 U16[2][NIT];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) U16[ks][it] = to_f16x8(U[2 * ks][it], U[2 * ks + 1][it]);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int t = 16 * tt + lr;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[tt][it][r] *= sm.gam[16 * tt + 4 * lg + r];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (32 * ks > 16 * tt + 15) continue;
-          const f16x8 av = lds_perm(&sm.tt.pqk[t * kTS + 32 * ks], lg);
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) O[tt][it] = mfma16x16x32(av, U16[ks][it], O[tt][it]);
-        }
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 16 * tt + 4 * lg + r;
-            if (row < nv)
-              store1<TO>(a.o, (static_cast<size_t>(c0 + row) * a.h_v + h) * D + w * IW + 16 * it + lr,
-                         a.scale * O[tt][it][r]);
-          }
-      }
-    }
+    // V of the next chunk is only read by its block solve: issue it here
+    if (more) prefetch_v(c0 + kC);
 
     // ---- S^T <- e^{G_C} S^T + K^T diag(e^{G_C-G}) U -----------------------
     {
-      f16x8 UD[2][NIT];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          f32x4 lo = U[2 * ks][it], hi = U[2 * ks + 1][it];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            lo[r] *= sm.dec[32 * ks + 4 * lg + r];
-            hi[r] *= sm.dec[32 * ks + 16 + 4 * lg + r];
-          }
-          UD[ks][it] = to_f16x8(lo, hi);
-        }
       const float gC = sm.gam[kC - 1];
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) {
-        const _Float16* krow = &sm.kt[(16 * jt + lr) * kTS];
+        SR_SCHED_FENCE();
+        const int j = 16 * jt + lr;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) S[jt][it] *= gC;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 av = lds_perm(krow + 32 * ks, lg);
+          f16x8 av;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            av[r] = sm.k[swz<D>(32 * ks + 4 * lg + r, j)];
+            av[4 + r] = sm.k[swz<D>(32 * ks + 16 + 4 * lg + r, j)];
+          }
 #pragma unroll
           for (int it = 0; it < NIT; ++it) S[jt][it] = mfma16x16x32(av, UD[ks][it], S[jt][it]);
         }
@@ -470,11 +518,13 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a) {
 
 template <int D, typename TI, typename TO>
 hipError_t launch3(const GdnArgs& a, hipStream_t s) {
-  dim3 grid(a.n_seqs * a.h_v), block(kThreads);
+  const int units = a.n_seqs * a.h_v;
+  const int per_xcd = (units + kXcd - 1) / kXcd;
+  dim3 grid(per_xcd * kXcd), block(kThreads);
   if (a.erase)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true>), grid, block, 0, s, a, per_xcd);
   else
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false>), grid, block, 0, s, a, per_xcd);
   return hipGetLastError();
 }
 
