@@ -65,6 +65,9 @@ int sr_gdn_replay_state(const sr_gdn_desc* d, const sr_gdn_io* io, void* stream)
     // the chunked kernel reads 16-byte rows of q, k and v
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
     if (!al16(a.k) || !al16(a.v) || (a.o && !al16(a.q))) return SR_EINVAL;
+    // outputs are written 4 values at a time
+    const uintptr_t omask = d->dtype_o == SR_F32 ? 15u : 7u;
+    if (a.o && (reinterpret_cast<uintptr_t>(a.o) & omask) != 0) return SR_EINVAL;
     e = sr::launch_gdn_chunk(a, s);
   } else if (sr::gdn_serial_supports(d->d_k, d->d_v)) {
     e = sr::launch_gdn_serial(a, s);

@@ -44,12 +44,12 @@ constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
 
 template <int D>
 struct ChunkSmem {
-  static constexpr int kWS = D + 4;  // fp16 row stride of -W
+  static constexpr int kWS = D + 8;  // fp16 row stride of V / -W
   static constexpr int kKS = D + 8;  // fp16 row stride of the K and Q rows
   _Float16 k[kC * kKS];              // K rows
   _Float16 q[kC * kKS];              // Q rows
   float a[kC * kAS];                 // A, fp32 (strictly lower blocks)
-  _Float16 w[kC * kWS];              // -W
+  _Float16 w[kC * kWS];              // V rows at staging, overwritten by -W
   _Float16 pqk[kC * kPS];            // P o (Q K^T)
   _Float16 td[4 * 16 * 16];          // (I + A_bb)^{-1}, row-major per block
   float gcum[kC];                    // G_t
@@ -96,7 +96,7 @@ __device__ __forceinline__ _Float16 raw_to_f16<F16>(uint16_t b) {
   return __builtin_bit_cast(_Float16, b);
 }
 
-template <int D, typename TI, typename TO, bool ERASE>
+template <int D, typename TI, typename TO, bool ERASE, bool WANT_O>
 __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
   constexpr int IW = D / 4;       // value (and key) columns per wave
   constexpr int NIT = IW / 16;    // 16-wide column tiles per wave
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
   const int g = h / (a.h_v / a.h_k);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
-  const bool want_o = a.o != nullptr;
+  constexpr bool want_o = WANT_O;
   const size_t qk_row = static_cast<size_t>(a.h_k) * D;  // elements per token
   const size_t v_row = static_cast<size_t>(a.h_v) * D;
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(g) * D;
@@ -155,11 +155,9 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
   // ---- prefetch registers (raw input bits) for the next chunk -------------
   // Addresses are a uniform row base (scalar registers) plus a per-lane
   // offset that does not change between chunks.
-  u16x8 pk[NPF], pq[NPF];
-  u16x4 pv[4][NIT];      // V in accumulator layout: rows 16bi+4lg+r, column lr
+  u16x8 pk[NPF], pq[NPF], pv[NPF];
   float pa = 0.0f, pb = 0.0f;
   auto kq_lane = [&]() { return ((w * kWave + l) / CPR) * static_cast<int>(qk_row) + 8 * ((w * kWave + l) % CPR); };
-  auto v_lane = [&]() { return 4 * lg * static_cast<int>(v_row) + w * IW + lr; };
   auto prefetch_kq = [&](int c0n) {
     const int nvn = min(kC, t_end - c0n);
 #pragma unroll
@@ -189,14 +187,12 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
   auto prefetch_v = [&](int c0n) {
     const int nvn = min(kC, t_end - c0n);
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint16_t* vb = vg + static_cast<size_t>(c0n + 16 * bi + r) * v_row;
-        const bool ok = 16 * bi + 4 * lg + r < nvn;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) pv[bi][it][r] = ok ? vb[v_lane() + 16 * it] : uint16_t(0);
-      }
+    for (int e = 0; e < NPF; ++e) {
+      const int row = (w * kWave + l) / CPR + (kThreads / CPR) * e;
+      const uint16_t* vb = vg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * v_row;
+      pv[e] = u16x8{};
+      if (row < nvn) pv[e] = *reinterpret_cast<const u16x8*>(vb + ((w * kWave + l) / CPR) * static_cast<int>(v_row) + 8 * ((w * kWave + l) % CPR));
+    }
   };
   if (t_begin < t_end) {
     prefetch_kq(t_begin);
@@ -231,6 +227,10 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
       const int dst = swz<D>(row, 8 * ch);
       *reinterpret_cast<f16x8*>(&sm.k[dst]) = kv;
       if (want_o) *reinterpret_cast<f16x8*>(&sm.q[dst]) = qv;
+      f16x8 vv;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) vv[x] = raw_to_f16<TI>(pv[e][x]);
+      *reinterpret_cast<f16x8*>(&sm.w[row * kWS + 8 * ch]) = vv;
     }
     if (w == 0) {
       float gl = 0.0f;
@@ -257,12 +257,18 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
 
     // the next chunk's K, Q and gates fly while this one computes
     const bool more = c0 + kC < t_end;
-    if (more) prefetch_kq(c0 + kC);
+    if (more) {
+      prefetch_kq(c0 + kC);
+      prefetch_v(c0 + kC);
+    }
 
     // ---- A (erase) and P o QK^T: lower-triangular 16x16 tiles -------------
     {
-      const int njobs = (ERASE ? 10 : 0) + (want_o ? 10 : 0);
-      for (int job = w; job < njobs; job += 4) {
+      constexpr int njobs = (ERASE ? 10 : 0) + (WANT_O ? 10 : 0);
+#pragma unroll
+      for (int jw = 0; jw < (njobs + 3) / 4; ++jw) {
+        const int job = w + 4 * jw;
+        if (job >= njobs) break;
         const bool is_kk = ERASE && job < 10;
         const int tj = job % 10;
         const int tr = tj < 1 ? 0 : tj < 3 ? 1 : tj < 6 ? 2 : 3;
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
           for (int r = 0; r < 4; ++r) {
             const int t = 16 * bi + 4 * lg + r;
             X[ct][r] = static_cast<float>(sm.k[swz<D>(t, j)]) * sm.bg[t];
-            X[NIT + ct][r] = static_cast<float>(raw_to_f16<TI>(pv[bi][ct][r])) * sm.beta[t];
+            X[NIT + ct][r] = static_cast<float>(sm.w[t * kWS + j]) * sm.beta[t];
           }
         }
         const float* arow = &sm.a[(16 * bi + lr) * kAS];
@@ -380,8 +386,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
         for (int it = 0; it < NIT; ++it)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            U[tt][it][r] =
-                static_cast<float>(raw_to_f16<TI>(pv[tt][it][r])) * sm.beta[16 * tt + 4 * lg + r];
+            U[tt][it][r] = static_cast<float>(sm.w[(16 * tt + 4 * lg + r) * kWS + w * IW + 16 * it + lr]) *
+                           sm.beta[16 * tt + 4 * lg + r];
     }
 
     // ---- U = U~ - W S^T, one key k-step at a time -------------------------
@@ -422,11 +428,13 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
         if (want_o) asm volatile("" : "+v"(U16[ks][it]));
       }
 
-    // ---- O = diag(e^G) Q S^T + (P o Q K^T) U, two token tiles at a time ----
+    // ---- O^T = S Q^T diag(e^G) + U^T (P o Q K^T)^T, two token tiles at a
+    // time.  Computing the transpose puts 4 consecutive value columns of one
+    // token in each lane, so every lane stores 8 contiguous bytes.
     if (want_o) {
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        f32x4 O[2][NIT];
+        f32x4 O[2][NIT];  // tile (u, it): value rows w*IW+16it+4lg+r, token column
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -440,10 +448,10 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int t = 16 * (2 * tp + u) + lr;
-            const f16x8 qa = cat44(lds4(&sm.q[swz<D>(t, 32 * kk + 4 * lg)]),
+            const f16x8 qb = cat44(lds4(&sm.q[swz<D>(t, 32 * kk + 4 * lg)]),
                                    lds4(&sm.q[swz<D>(t, 32 * kk + 16 + 4 * lg)]));
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(qa, s16[it], O[u][it]);
+            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(s16[it], qb, O[u][it]);
           }
         }
 #pragma unroll
@@ -451,33 +459,25 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
           SR_SCHED_FENCE();
           const int tt = 2 * tp + u;
           const int t = 16 * tt + lr;
+          const float gt = sm.gam[t];
 #pragma unroll
-          for (int it = 0; it < NIT; ++it)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O[u][it][r] *= sm.gam[16 * tt + 4 * lg + r];
+          for (int it = 0; it < NIT; ++it) O[u][it] *= gt;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             if (32 * ks > 16 * tt + 15) continue;  // P o QK^T is lower triangular
             const _Float16* pr = &sm.pqk[t * kPS + 32 * ks];
-            const f16x8 av = cat44(lds4(pr + 4 * lg), lds4(pr + 16 + 4 * lg));
+            const f16x8 pb = cat44(lds4(pr + 4 * lg), lds4(pr + 16 + 4 * lg));
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(av, U16[ks][it], O[u][it]);
+            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(U16[ks][it], pb, O[u][it]);
           }
+          if (t < nv) {
+            const size_t ob = (static_cast<size_t>(c0 + t) * a.h_v + h) * D + w * IW + 4 * lg;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const size_t ob = (static_cast<size_t>(c0 + 16 * tt + r) * a.h_v + h) * D;
-            if (16 * tt + 4 * lg + r < nv) {
-#pragma unroll
-              for (int it = 0; it < NIT; ++it)
-                store1<TO>(a.o, ob + v_lane() + 16 * it, a.scale * O[u][it][r]);
-            }
+            for (int it = 0; it < NIT; ++it) store4<TO>(a.o, ob + 16 * it, a.scale * O[u][it]);
           }
         }
       }
     }
-
-    // V of the next chunk is only read by its block solve: issue it here
-    if (more) prefetch_v(c0 + kC);
 
     // ---- S^T <- e^{G_C} S^T + K^T diag(e^{G_C-G}) U -----------------------
     {
@@ -521,10 +521,15 @@ hipError_t launch3(const GdnArgs& a, hipStream_t s) {
   const int units = a.n_seqs * a.h_v;
   const int per_xcd = (units + kXcd - 1) / kXcd;
   dim3 grid(per_xcd * kXcd), block(kThreads);
-  if (a.erase)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true>), grid, block, 0, s, a, per_xcd);
+  const bool o = a.o != nullptr;
+  if (a.erase && o)
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true>), grid, block, 0, s, a, per_xcd);
+  else if (a.erase)
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, false>), grid, block, 0, s, a, per_xcd);
+  else if (o)
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, true>), grid, block, 0, s, a, per_xcd);
   else
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, false>), grid, block, 0, s, a, per_xcd);
   return hipGetLastError();
 }
 

@@ -90,6 +90,28 @@ __device__ __forceinline__ void store1<F32>(void* base, size_t idx, float v) {
   reinterpret_cast<float*>(base)[idx] = v;
 }
 
+// Store 4 consecutive values of the output type (8- or 16-byte aligned).
+template <typename T>
+__device__ __forceinline__ void store4(void* base, size_t idx, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<BF16>(void* base, size_t idx, f32x4 v) {
+  u16x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = f32_to_bf16(v[e]);
+  *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(base) + idx) = r;
+}
+template <>
+__device__ __forceinline__ void store4<F16>(void* base, size_t idx, f32x4 v) {
+  f16x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = static_cast<_Float16>(v[e]);
+  *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(base) + idx) = r;
+}
+template <>
+__device__ __forceinline__ void store4<F32>(void* base, size_t idx, f32x4 v) {
+  *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + idx) = v;
+}
+
 // Read one element as fp32.
 template <typename T>
 __device__ __forceinline__ float load1(const void* base, size_t idx);
