@@ -179,7 +179,8 @@ int sr_gather_suffix(const void* pool, int32_t hidden, int32_t elem_bytes,
  *               final_state above)
  *   conv_states [n_gdn][n_seqs][conv_dim][conv_width-1] fp32 or NULL: the
  *               last conv_width-1 pre-conv rows of q|k|v per sequence,
- *               oldest first, zero where a sequence is shorter
+ *               oldest first, zero where a sequence is shorter (asking for
+ *               them makes the last layer project its q columns too)
  *   workspace   >= sr_replay_group_workspace_bytes(desc) bytes, 256-aligned
  *
  * Supported: h_v % h_k == 0, d in {64, 128}, conv_width in 2..8,
