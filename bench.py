@@ -110,6 +110,109 @@ def cpu_baseline(case, budget_s=20.0):
                       f"heads), fp64 token loop, {t:.2f} s"}
 
 
+def group_flops(T, hidden, h_k, h_v, d, n_gdn, chunk=64):
+    """Nominal matrix-core FLOPs of one group replay: projections, the chunked
+    recurrence (outputs for all but the last layer) and output projections."""
+    n_in = 2 * h_k * d + 2 * h_v * d + 2 * h_v
+    n_last = (h_k + h_v) * d + 2 * h_v
+    f = 0.0
+    for li in range(n_gdn):
+        last = li == n_gdn - 1
+        f += 2.0 * T * hidden * (n_last if last else n_in)
+        _, fl = gdn_algorithmic(1, T, h_k, h_v, d, want_o=not last)
+        f += fl
+        if not last:
+            f += 2.0 * T * h_v * d * hidden
+    return f
+
+
+def timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_group(steps, warmup, to_dev):
+    """3-layer replay group (hidden 2560) from 4 x 1638 anchors, and the
+    varlen path: 64 hits gathered from a paged pool of full prefixes and
+    replayed through the same group shapes."""
+    import numpy as np
+    import torch
+    import linear_attention_state_anchor_amd as sr
+    from replay_inputs import PAGE, config_c4, config_c5
+
+    out = {}
+    g = config_c4()
+    packed = [sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), 16, 32, 128)
+              for w in g.weights]
+    anchors, cu = to_dev(g.anchors), to_dev(g.cu_seqlens)
+    T = g.total_tokens
+    states = torch.empty((3, g.n_seqs, 32, 128, 128), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty((1 << 20,), dtype=torch.uint8, device="cuda:0")
+    sr.replay_group(anchors, packed, cu, g.layer_kind, 16, 32, 128, states=states)
+    import ctypes
+    from linear_attention_state_anchor_amd import _lib
+    kinds = (ctypes.c_int32 * 4)(*g.layer_kind)
+    desc = _lib.GroupDesc(4, ctypes.cast(kinds, ctypes.POINTER(ctypes.c_int32)), 2560, 16, 32,
+                          128, 4, 1e-6, 1e-6, g.n_seqs, T, T)
+    wsb = int(_lib.load().sr_replay_group_workspace_bytes(ctypes.byref(desc)))
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda:0")
+    ms = timed(lambda: sr.replay_group(anchors, packed, cu, g.layer_kind, 16, 32, 128,
+                                       states=states, workspace=ws), steps, warmup)
+    fl = group_flops(T, 2560, 16, 32, 128, 3)
+    out["group"] = {
+        "workload": "3 GDN layers + skipped FA, hidden 2560, 4 requests x 1638 anchors "
+                    "(5% of 32K), bf16 anchors and weights",
+        "ms_per_step": ms, "replayed_tokens_per_s_per_layer": 3 * T / (ms / 1e3),
+        "tflops": fl / (ms / 1e3) / 1e12, "mfma_frac": fl / (ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFS,
+    }
+    del ws
+    # varlen: gather + group
+    pc, wts = config_c5()
+    packed5 = [sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), 16, 32, 128)
+               for w in wts]
+    gen = torch.Generator(device="cuda:0").manual_seed(105)
+    pool = torch.randn((pc.n_pages, PAGE, 2560), generator=gen, device="cuda:0",
+                       dtype=torch.float32).to(torch.bfloat16)
+    pt, ml, sl = to_dev(pc.page_table), to_dev(pc.matched_len), to_dev(pc.suffix_len)
+    T5 = int(pc.suffix_len.sum())
+    packed_anchors = torch.empty((T5, 2560), dtype=torch.bfloat16, device="cuda:0")
+    cu5 = torch.empty((65,), dtype=torch.int32, device="cuda:0")
+    desc5 = _lib.GroupDesc(4, ctypes.cast(kinds, ctypes.POINTER(ctypes.c_int32)), 2560, 16, 32,
+                           128, 4, 1e-6, 1e-6, 64, T5, int(pc.suffix_len.max()))
+    ws5 = torch.empty((int(_lib.load().sr_replay_group_workspace_bytes(ctypes.byref(desc5))),),
+                      dtype=torch.uint8, device="cuda:0")
+    states5 = torch.empty((3, 64, 32, 128, 128), dtype=torch.float32, device="cuda:0")
+    gather = lambda: sr.gather_suffix(pool, pt, ml, sl, T5, packed=packed_anchors, cu_seqlens=cu5)
+    ms_g = timed(gather, steps, warmup)
+    def path():
+        gather()
+        sr.replay_group(packed_anchors, packed5, cu5, [0, 0, 0, 1], 16, 32, 128,
+                        states=states5, workspace=ws5)
+    ms_p = timed(path, max(2, steps // 5), 1)
+    fl5 = group_flops(T5, 2560, 16, 32, 128, 3)
+    gb = 2 * T5 * 2560 * 2 / 1e9
+    out["varlen"] = {
+        "workload": f"64 hits, m ~ U{{8192..32768}}, k = ceil(r m), r ~ U[0.05,0.10] "
+                    f"(T = {T5}), gather from 64-token pages + 3-layer group, hidden 2560",
+        "ms_per_step": ms_p, "replayed_tokens_per_s_per_layer": 3 * T5 / (ms_p / 1e3),
+        "tflops": fl5 / (ms_p / 1e3) / 1e12,
+        "gather_ms": ms_g, "gather_gbs": gb / (ms_g / 1e3),
+        "gather_hbm_frac": gb / (ms_g / 1e3) / HBM_PEAK_GBS,
+    }
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +220,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-group", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="after timing, run one 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the replay "
@@ -202,8 +308,15 @@ def main():
             "bytes_per_launch": byts,
         },
     }
+    if not args.no_group:
+        line.update(bench_group(max(3, args.steps // 5), 2, to_dev))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    if args.copy_calib:
+        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(line), flush=True)
 
 
