@@ -213,6 +213,52 @@ def bench_group(steps, warmup, to_dev):
     return out
 
 
+def error_vs_k(to_dev, n_req=8, ks=(16, 32, 64, 128, 256, 512)):
+    """Replay error against the replay length (untimed report).
+
+    For n_req hits of the varlen workload, the full-prefix state of every GDN
+    layer (Eq. 1: the state is a function of all m inputs) is rebuilt from all
+    m anchors, and compared with the suffix replay of the last k anchors (Eq. 2)
+    for k in ks and k = ceil(0.05 m), ceil(0.10 m).  Relative Frobenius error
+    per layer, over all heads of the n_req requests."""
+    import math
+    import numpy as np
+    import torch
+    import linear_attention_state_anchor_amd as sr
+    from replay_inputs import PAGE, config_c5
+
+    pc, wts = config_c5()
+    packed = [sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), 16, 32, 128)
+              for w in wts]
+    gen = torch.Generator(device="cuda:0").manual_seed(105)
+    pool = torch.randn((pc.n_pages, PAGE, 2560), generator=gen, device="cuda:0",
+                       dtype=torch.float32).to(torch.bfloat16)
+    sel = list(range(n_req))
+    m = pc.matched_len[sel].astype(np.int32)
+    pt = to_dev(np.ascontiguousarray(pc.page_table[sel]))
+    ml = to_dev(m)
+
+    def states_for(klist):
+        kk = np.minimum(np.asarray(klist, np.int32), m)
+        anchors, cu = sr.gather_suffix(pool, pt, ml, to_dev(kk), int(kk.sum()))
+        S = sr.replay_group(anchors, packed, cu, [0, 0, 0, 1], 16, 32, 128,
+                            max_seqlen=int(kk.max()))
+        return S.double()
+
+    full = states_for(m)
+    rows = []
+    for label, klist in ([(str(k), [k] * n_req) for k in ks] +
+                         [("ceil(0.05m)", [math.ceil(0.05 * int(x)) for x in m]),
+                          ("ceil(0.10m)", [math.ceil(0.10 * int(x)) for x in m])]):
+        S = states_for(klist)
+        err = [float(torch.linalg.vector_norm(S[l] - full[l]) / torch.linalg.vector_norm(full[l]))
+               for l in range(full.shape[0])]
+        rows.append({"k": label, "rel_fro_per_layer": err})
+    return {"workload": f"{n_req} hits of the varlen workload (m = {list(map(int, m))}), "
+                        "3-layer group, full-prefix vs suffix replay, all on the GPU",
+            "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +267,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-group", action="store_true")
+    ap.add_argument("--error-vs-k", action="store_true",
+                    help="print the replay-error-vs-k report (untimed) instead of the benchmark")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after timing, run one 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -239,6 +287,10 @@ def main():
         if x.dtype == np.uint16:  # bf16 bit patterns
             return torch.from_numpy(x.view(np.int16)).to("cuda:0").view(torch.bfloat16)
         return torch.from_numpy(x).to("cuda:0")
+
+    if args.error_vs_k:
+        print(json.dumps({"error_vs_k": error_vs_k(to_dev)}), flush=True)
+        return
 
     case = config_c3()
     n, L, hk, hv, d = case.n_seqs, 3276, case.h_k, case.h_v, case.d_k
