@@ -77,6 +77,22 @@ __device__ __forceinline__ f32x4 mfma16x16x16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+  x += dpp_f32<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_f32<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_f32<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_f32<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_f32<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_f32<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // Keeps the scheduler from hoisting the loads of later unrolled iterations
 // above this point (which would make their registers live all at once).
 #define SR_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -94,6 +110,85 @@ __device__ __forceinline__ _Float16 raw_to_f16<BF16>(uint16_t b) {
 template <>
 __device__ __forceinline__ _Float16 raw_to_f16<F16>(uint16_t b) {
   return __builtin_bit_cast(_Float16, b);
+}
+
+// Tile jobs of wave W for one chunk: the diagonal block A_WW (erase mode)
+// followed by the inverse (I + A_WW)^{-1}, then every fourth of the
+// off-diagonal A tiles and the lower P o QK^T tiles.  The job list is fixed at
+// compile time so the whole section is straight-line code with immediate
+// LDS offsets, and the k-steps of all jobs interleave.
+//   A tile jobs:        (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+//   P o QK^T tile jobs: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+template <int D, bool ERASE, bool WANT_O, int W>
+__device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
+  constexpr int NKJ = D / 32;
+  constexpr int kJob[16][3] = {{1, 1, 0}, {1, 2, 0}, {1, 2, 1}, {1, 3, 0}, {1, 3, 1}, {1, 3, 2},
+                               {0, 0, 0}, {0, 1, 0}, {0, 1, 1}, {0, 2, 0}, {0, 2, 1}, {0, 2, 2},
+                               {0, 3, 0}, {0, 3, 1}, {0, 3, 2}, {0, 3, 3}};
+  // slot 0: the diagonal A block; slots 1..4: jobs W, W+4, W+8, W+12
+  auto slot_on = [](int q) constexpr {
+    if (q == 0) return ERASE;
+    const int j = W + 4 * (q - 1);
+    return kJob[j][0] == 1 ? ERASE : WANT_O;
+  };
+  auto slot_kk = [](int q) constexpr { return q == 0 || kJob[W + 4 * (q - 1)][0] == 1; };
+  auto slot_tr = [](int q) constexpr { return q == 0 ? W : kJob[W + 4 * (q - 1)][1]; };
+  auto slot_tc = [](int q) constexpr { return q == 0 ? W : kJob[W + 4 * (q - 1)][2]; };
+  f32x4 acc[5];
+#pragma unroll
+  for (int q = 0; q < 5; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < NKJ; ++ks) {
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      if (!slot_on(q)) continue;
+      const _Float16* xa = slot_kk(q) ? sm.k : sm.q;
+      const f16x8 av = lds8(&xa[swz<D>(16 * slot_tr(q) + lr, 32 * ks + 8 * lg)]);
+      const f16x8 bv = lds8(&sm.k[swz<D>(16 * slot_tc(q) + lr, 32 * ks + 8 * lg)]);
+      acc[q] = mfma16x16x32(av, bv, acc[q]);
+    }
+  }
+  // epilogues: masked, decay-weighted tiles to LDS; the diagonal A block
+  // stays in registers for the inverse
+  f32x4 diag = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    if (!slot_on(q)) continue;
+    const int col = 16 * slot_tc(q) + lr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * slot_tr(q) + 4 * lg + r;
+      const float dgam = __expf(sm.gcum[row] - sm.gcum[col]);
+      if (q == 0)
+        diag[r] = row > col ? sm.beta[row] * dgam * acc[q][r] : 0.0f;
+      else if (slot_kk(q))
+        sm.a[row * kAS + col] = row > col ? sm.beta[row] * dgam * acc[q][r] : 0.0f;
+      else
+        sm.pqk[row * kPS + col] = static_cast<_Float16>(row >= col ? dgam * acc[q][r] : 0.0f);
+    }
+  }
+  if (ERASE) {
+    // (I + A_WW)^{-1} by forward substitution in fp32, lane column lr.
+    // Entry (r, m) of the block sits in lane m + 16 (r / 4), register r % 4
+    // of the diagonal accumulator; v_readlane broadcasts it as a scalar.
+    const int c = lr;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float t = (r == c) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) {
+        const float lrm = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(diag[r % 4]), m + 16 * (r / 4)));
+        t = fmaf(-lrm, x[m], t);
+      }
+      x[r] = t;
+    }
+    if (lg == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.td[W * 256 + r * 16 + c] = static_cast<_Float16>(x[r]);
+    }
+  }
 }
 
 template <int D, typename TI, typename TO, bool ERASE, bool WANT_O>
@@ -194,9 +289,37 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
       if (row < nvn) pv[e] = *reinterpret_cast<const u16x8*>(vb + ((w * kWave + l) / CPR) * static_cast<int>(v_row) + 8 * ((w * kWave + l) % CPR));
     }
   };
+  // Converts the prefetched raw inputs to fp16 in place and scans the next
+  // chunk's log-decays (wave 0, lane = token), once the loads have landed.
+  float n_g = 0.0f, n_eg = 1.0f, n_dec = 1.0f, n_be = 0.0f;
+  auto prepare = [&](int c0n) {
+    const int nvn = min(kC, t_end - c0n);
+#pragma unroll
+    for (int e = 0; e < NPF; ++e)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        pk[e][x] = f16_bits(raw_to_f16<TI>(pk[e][x]));
+        pq[e][x] = f16_bits(raw_to_f16<TI>(pq[e][x]));
+        pv[e][x] = f16_bits(raw_to_f16<TI>(pv[e][x]));
+      }
+    if (w == 0) {
+      float gl = 0.0f;
+      if (l < nvn) {
+        gl = a.alpha_is_log ? pa : __logf(pa);
+        gl = fmaxf(gl, -64.0f);
+      }
+      n_be = l < nvn ? pb : 0.0f;
+      gl = wave_inclusive_sum(gl);
+      const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), kWave - 1));
+      n_g = gl;
+      n_eg = __expf(gl);
+      n_dec = __expf(gC - gl);
+    }
+  };
   if (t_begin < t_end) {
     prefetch_kq(t_begin);
     prefetch_v(t_begin);
+    prepare(t_begin);
   }
 
   for (int c0 = t_begin; c0 < t_end; c0 += kC) {
@@ -213,45 +336,22 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
       lg = (t_ / 16) % 4;
     }
 
-    // ---- stage this chunk: K, Q rows to LDS; gate scalars ----------------
+    // ---- stage this chunk: K, Q, V rows (already fp16) and gate scalars --
 #pragma unroll
     for (int e = 0; e < NPF; ++e) {
       const int item = w * kWave + l + kThreads * e;
       const int row = item / CPR, ch = item % CPR;
-      f16x8 kv, qv;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        kv[x] = raw_to_f16<TI>(pk[e][x]);
-        qv[x] = raw_to_f16<TI>(pq[e][x]);
-      }
       const int dst = swz<D>(row, 8 * ch);
-      *reinterpret_cast<f16x8*>(&sm.k[dst]) = kv;
-      if (want_o) *reinterpret_cast<f16x8*>(&sm.q[dst]) = qv;
-      f16x8 vv;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) vv[x] = raw_to_f16<TI>(pv[e][x]);
-      *reinterpret_cast<f16x8*>(&sm.w[row * kWS + 8 * ch]) = vv;
+      *reinterpret_cast<u16x8*>(&sm.k[dst]) = pk[e];
+      if (want_o) *reinterpret_cast<u16x8*>(&sm.q[dst]) = pq[e];
+      *reinterpret_cast<u16x8*>(&sm.w[row * kWS + 8 * ch]) = pv[e];
     }
     if (w == 0) {
-      float gl = 0.0f;
-      if (l < nv) {
-        gl = a.alpha_is_log ? pa : __logf(pa);
-        gl = fmaxf(gl, -64.0f);
-      }
-      const float be = l < nv ? pb : 0.0f;
-      // inclusive prefix sum of the log-decays over the 64 lanes
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const float y = __shfl_up(gl, off, kWave);
-        if (l >= off) gl += y;
-      }
-      const float gC = __shfl(gl, kWave - 1, kWave);
-      const float e_g = __expf(gl);
-      sm.gcum[l] = gl;
-      sm.gam[l] = e_g;
-      sm.dec[l] = __expf(gC - gl);
-      sm.beta[l] = be;
-      sm.bg[l] = be * e_g;
+      sm.gcum[l] = n_g;
+      sm.gam[l] = n_eg;
+      sm.dec[l] = n_dec;
+      sm.beta[l] = n_be;
+      sm.bg[l] = n_be * n_eg;
     }
     __syncthreads();
 
@@ -263,35 +363,14 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
     }
 
     // ---- A (erase) and P o QK^T: lower-triangular 16x16 tiles -------------
-    {
-      constexpr int njobs = (ERASE ? 10 : 0) + (WANT_O ? 10 : 0);
-#pragma unroll
-      for (int jw = 0; jw < (njobs + 3) / 4; ++jw) {
-        const int job = w + 4 * jw;
-        if (job >= njobs) break;
-        const bool is_kk = ERASE && job < 10;
-        const int tj = job % 10;
-        const int tr = tj < 1 ? 0 : tj < 3 ? 1 : tj < 6 ? 2 : 3;
-        const int tc = tj - tr * (tr + 1) / 2;
-        const _Float16* xa = is_kk ? sm.k : sm.q;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKJ; ++ks) {
-          const f16x8 av = lds8(&xa[swz<D>(16 * tr + lr, 32 * ks + 8 * lg)]);
-          const f16x8 bv = lds8(&sm.k[swz<D>(16 * tc + lr, 32 * ks + 8 * lg)]);
-          acc = mfma16x16x32(av, bv, acc);
-        }
-        const int col = 16 * tc + lr;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * tr + 4 * lg + r;
-          const float dgam = __expf(sm.gcum[row] - sm.gcum[col]);
-          if (is_kk)
-            sm.a[row * kAS + col] = row > col ? sm.beta[row] * dgam * acc[r] : 0.0f;
-          else
-            sm.pqk[row * kPS + col] = static_cast<_Float16>(row >= col ? dgam * acc[r] : 0.0f);
-        }
-      }
+    // Wave w first forms the diagonal block A_ww and inverts I + A_ww itself
+    // (wave-local LDS round trip, no barrier), then takes its share of the
+    // off-diagonal A tiles and the P o QK^T tiles.
+    switch (w) {
+      case 0: chunk_tiles<D, ERASE, WANT_O, 0>(sm, lr, lg); break;
+      case 1: chunk_tiles<D, ERASE, WANT_O, 1>(sm, lr, lg); break;
+      case 2: chunk_tiles<D, ERASE, WANT_O, 2>(sm, lr, lg); break;
+      default: chunk_tiles<D, ERASE, WANT_O, 3>(sm, lr, lg); break;
     }
     __syncthreads();
 
@@ -299,43 +378,17 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
     // w*IW + 16it..
     f32x4 U[4][NIT];
     if (ERASE) {
-      // ---- (I + A_bb)^{-1} for diagonal block b = w, fp32 ----------------
-      {
-        const int c = lr;
-        const float* ab = &sm.a[(16 * w) * kAS + 16 * w];
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float acc = (r == c) ? 1.0f : 0.0f;
-#pragma unroll
-          for (int m = 0; m < r; ++m) acc = fmaf(-ab[r * kAS + m], x[m], acc);
-          x[r] = acc;
-        }
-        if (lg == 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sm.td[w * 256 + r * 16 + c] = static_cast<_Float16>(x[r]);
-        }
-      }
-      __syncthreads();
-
       // ---- block forward substitution for [W | U~], this wave's columns --
       // column tile ct < NIT: W columns w*IW + 16ct (kept as -W in LDS);
       // ct >= NIT: U~ columns w*IW + 16(ct-NIT) (kept in U).  Earlier block
       // rows come back as fp16 B operands: W from LDS, U~ from registers.
+      f16x4 Wh[3][NIT];  // earlier block rows of W as fp16 operands
       auto yprev = [&](int m, int ct) -> f16x4 {
-        if (ct < NIT) {
-          const int j = w * IW + 16 * ct + lr;
-          f16x4 y;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) y[r] = -sm.w[(16 * m + 4 * lg + r) * kWS + j];
-          return y;
-        }
+        if (ct < NIT) return Wh[m][ct];
         return to_f16x4(U[m][ct - NIT]);
       };
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
-        SR_SCHED_FENCE();
         f32x4 X[2 * NIT];
 #pragma unroll
         for (int ct = 0; ct < NIT; ++ct) {
@@ -370,9 +423,11 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
           const f32x4 y = mfma16x16x16(t4, to_f16x4(X[ct]), f32x4{0.f, 0.f, 0.f, 0.f});
           if (ct < NIT) {
             const int j = w * IW + 16 * ct + lr;
+            const f16x4 yh = to_f16x4(y);
+            if (bi < 3) Wh[bi][ct] = yh;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              sm.w[(16 * bi + 4 * lg + r) * kWS + j] = static_cast<_Float16>(-y[r]);
+              sm.w[(16 * bi + 4 * lg + r) * kWS + j] = -yh[r];
           } else {
             U[bi][ct - NIT] = y;
           }
@@ -441,7 +496,6 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
           for (int it = 0; it < NIT; ++it) O[u][it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKJ; ++kk) {
-          SR_SCHED_FENCE();
           f16x8 s16[NIT];
 #pragma unroll
           for (int it = 0; it < NIT; ++it) s16[it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
@@ -456,7 +510,6 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          SR_SCHED_FENCE();
           const int tt = 2 * tp + u;
           const int t = 16 * tt + lr;
           const float gt = sm.gam[t];
@@ -501,6 +554,7 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
         }
       }
     }
+    if (more) prepare(c0 + kC);
     __syncthreads();  // LDS reused by the next chunk
   }
 
