@@ -25,11 +25,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
+// fp32 -> bf16 bits, round to nearest even (the gfx950 conversion
+// instruction, which pairs up neighbouring conversions).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ uint16_t f16_bits(_Float16 h) {
@@ -95,10 +94,11 @@ template <typename T>
 __device__ __forceinline__ void store4(void* base, size_t idx, f32x4 v);
 template <>
 __device__ __forceinline__ void store4<BF16>(void* base, size_t idx, f32x4 v) {
-  u16x4 r;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 r;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = f32_to_bf16(v[e]);
-  *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(base) + idx) = r;
+  for (int e = 0; e < 4; ++e) r[e] = static_cast<__bf16>(v[e]);
+  *reinterpret_cast<bf16x4*>(reinterpret_cast<uint16_t*>(base) + idx) = r;
 }
 template <>
 __device__ __forceinline__ void store4<F16>(void* base, size_t idx, f32x4 v) {

@@ -101,12 +101,22 @@ def test_beta_zero_is_pure_decay_on_gpu():
     assert rel_fro(S[0, 0], decay * c.initial_state[0, 0].astype(np.float64)) < 1e-5
 
 
-def test_state_only_matches_full_run():
-    c = gdn_case([300, 77], 2, 4, 128, "bf16", seed=23, normalize_q=True)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_state_only_matches_full_run(d, dtype):
+    """State-only replay (the last layer of a group) equals the state of the
+    full run bit for bit and matches the oracle, for sequences whose last
+    chunk is full (64, 128) as well as ragged ones."""
+    c = gdn_case([300, 77, 64, 128], 2, 4, d, "bf16", seed=23, normalize_q=True)
+    if dtype == "f16":   # the same values stored as fp16 (bf16 -> fp16 is exact here)
+        f16 = lambda x: ((x.astype(np.uint32) << 16).view(np.float32)).astype(np.float16)
+        c.q, c.k, c.v = f16(c.q), f16(c.k), f16(c.v)
     S1, _ = gpu_run(c, want_o=True)
     S2, o2 = gpu_run(c, want_o=False)
     assert o2 is None
     np.testing.assert_array_equal(S1, S2)
+    Sr, _ = oracle_run(c, want_o=False)
+    assert rel_fro(S2, Sr) <= TOL_BF16
 
 
 @pytest.mark.parametrize("o_dtype", ["f32", "f16"])
