@@ -52,6 +52,7 @@ struct ChunkSmem {
   uint16_t w[kC * kWS];              // raw V rows at staging, overwritten by -W (fp16)
   _Float16 pqk[kC * kPS];            // P o (Q K^T)
   _Float16 td[4 * 16 * 16];          // (I + A_bb)^{-1}, row-major per block
+  float dg[4 * 16 * 16];             // A_bb, fp32, row-major per block
   float gcum[kC];                    // G_t
   float gam[kC];                     // e^{G_t}
   float dec[kC];                     // e^{G_C - G_t}
@@ -200,9 +201,8 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
       acc[q] = mfma16x16x32(av, bv, acc[q]);
     }
   }
-  // epilogues: masked, decay-weighted tiles to LDS; the diagonal A block
-  // stays in registers for the inverse
-  f32x4 diag = {0.f, 0.f, 0.f, 0.f};
+  // epilogues: masked, decay-weighted tiles to LDS (the diagonal A block in
+  // fp32 for the inverse)
 #pragma unroll
   for (int q = 0; q < 5; ++q) {
     if (!slot_on(q)) continue;
@@ -212,7 +212,7 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
       const int row = 16 * slot_tr(q) + 4 * lg + r;
       const float dgam = __expf(sm.gcum[row] - sm.gcum[col]);
       if (q == 0)
-        diag[r] = row > col ? sm.beta[row] * dgam * acc[q][r] : 0.0f;
+        sm.dg[W * 256 + (4 * lg + r) * 16 + lr] = row > col ? sm.beta[row] * dgam * acc[q][r] : 0.0f;
       else if (slot_kk(q))
         sm.a[row * kAS + col] = static_cast<_Float16>(row > col ? -(sm.beta[row] * dgam * acc[q][r]) : 0.0f);
       else
@@ -220,20 +220,17 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
     }
   }
   if (ERASE) {
-    // (I + A_WW)^{-1} by forward substitution in fp32, lane column lr.
-    // Entry (r, m) of the block sits in lane m + 16 (r / 4), register r % 4
-    // of the diagonal accumulator; v_readlane broadcasts it as a scalar.
+    // (I + A_WW)^{-1} by forward substitution in fp32, lane column lr; the
+    // block's rows come back from LDS as broadcast reads (this wave wrote
+    // them, so no barrier is needed)
     const int c = lr;
+    const float* ab = &sm.dg[W * 256];
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float t = (r == c) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) {
-        const float lrm = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(diag[r % 4]), m + 16 * (r / 4)));
-        t = fmaf(-lrm, x[m], t);
-      }
+      for (int m = 0; m < r; ++m) t = fmaf(-ab[r * 16 + m], x[m], t);
       x[r] = t;
     }
     if (lg == 0) {
