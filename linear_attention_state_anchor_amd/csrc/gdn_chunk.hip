@@ -44,10 +44,15 @@ constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
 
 template <int D>
 struct ChunkSmem {
-  static constexpr int kWS = D + 8;  // fp16 row stride of V / -W
-  static constexpr int kKS = D + 8;  // fp16 row stride of the K and Q rows
+  // Row strides (fp16 elements), chosen from measured LDS bank conflicts:
+  // K is read as 16-byte rows and by transpose reads (conflict-free with 16
+  // elements of padding); Q and V / -W are read as 8-byte rows and written as
+  // 2-byte columns (conflict-free, or nearly, with 8).
+  static constexpr int kKS = D + 16;  // K rows
+  static constexpr int kQS = D + 8;   // Q rows
+  static constexpr int kWS = D + 8;   // V / -W rows
   _Float16 k[kC * kKS];              // K rows
-  _Float16 q[kC * kKS];              // Q rows
+  _Float16 q[kC * kQS];              // Q rows
   _Float16 a[kC * kAS];              // -A (strictly lower off-diagonal blocks)
   uint16_t w[kC * kWS];              // raw V rows at staging, overwritten by -W (fp16)
   _Float16 pqk[kC * kPS];            // P o (Q K^T)
@@ -60,11 +65,14 @@ struct ChunkSmem {
   float bg[kC];                      // b_t e^{G_t}
 };
 
-// element (t, j) of a padded [64][D] fp16 row tile (rows 16-byte aligned,
-// consecutive rows 4 banks apart)
+// element (t, j) of the padded K and Q row tiles
 template <int D>
-__device__ __forceinline__ int swz(int t, int j) {
-  return t * (D + 8) + j;
+__device__ __forceinline__ int kidx(int t, int j) {
+  return t * ChunkSmem<D>::kKS + j;
+}
+template <int D>
+__device__ __forceinline__ int qidx(int t, int j) {
+  return t * ChunkSmem<D>::kQS + j;
 }
 
 __device__ __forceinline__ f16x8 lds8(const _Float16* p) {
@@ -195,9 +203,9 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
 #pragma unroll
     for (int q = 0; q < 5; ++q) {
       if (!slot_on(q)) continue;
-      const _Float16* xa = slot_kk(q) ? sm.k : sm.q;
-      const f16x8 av = lds8(&xa[swz<D>(16 * slot_tr(q) + lr, 32 * ks + 8 * lg)]);
-      const f16x8 bv = lds8(&sm.k[swz<D>(16 * slot_tc(q) + lr, 32 * ks + 8 * lg)]);
+      const f16x8 av = slot_kk(q) ? lds8(&sm.k[kidx<D>(16 * slot_tr(q) + lr, 32 * ks + 8 * lg)])
+                                  : lds8(&sm.q[qidx<D>(16 * slot_tr(q) + lr, 32 * ks + 8 * lg)]);
+      const f16x8 bv = lds8(&sm.k[kidx<D>(16 * slot_tc(q) + lr, 32 * ks + 8 * lg)]);
       acc[q] = mfma16x16x32(av, bv, acc[q]);
     }
   }
@@ -249,8 +257,6 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
   constexpr int CPR = D / 8;      // 16-byte chunks per row
   constexpr int NPF = CPR / 4;    // 16-byte K (and Q) row pieces per thread
   constexpr int kWS = ChunkSmem<D>::kWS;
-  // byte distance from the K tile to the V / -W tile
-  constexpr int kVOff = static_cast<int>(offsetof(ChunkSmem<D>, w) - offsetof(ChunkSmem<D>, k));
   static_assert(NIT >= 1, "D too small");
 
   __shared__ ChunkSmem<D> sm;
@@ -377,14 +383,15 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
     // that the many lane-dependent LDS/global addresses are recomputed in the
     // loop instead of being hoisted out of it (which would pin one register
     // per address for the whole sequence).
-    int tro;  // this lane's transpose-read offset in a [64][D + 8] row tile
+    int tro, trv;  // this lane's transpose-read offsets in the K and V tiles
     {
       int t_ = tid;
       asm volatile("" : "+v"(t_));
       l = t_ % kWave;
       lr = t_ % 16;
       lg = (t_ / 16) % 4;
-      tro = (l / 4) * (D + 8) + 4 * (l % 4);
+      tro = (l / 4) * ChunkSmem<D>::kKS + 4 * (l % 4);
+      trv = (l / 4) * kWS + 4 * (l % 4);
     }
 
     // ---- stage this chunk: K, Q, V rows (already fp16) and gate scalars --
@@ -392,9 +399,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
     for (int e = 0; e < NPF; ++e) {
       const int item = w * kWave + l + kThreads * e;
       const int row = item / CPR, ch = item % CPR;
-      const int dst = swz<D>(row, 8 * ch);
-      *reinterpret_cast<u16x8*>(&sm.k[dst]) = pk[e];
-      if (want_o) *reinterpret_cast<u16x8*>(&sm.q[dst]) = pq[e];
+      *reinterpret_cast<u16x8*>(&sm.k[kidx<D>(row, 8 * ch)]) = pk[e];
+      if (want_o) *reinterpret_cast<u16x8*>(&sm.q[qidx<D>(row, 8 * ch)]) = pq[e];
       *reinterpret_cast<u16x8*>(&sm.w[row * kWS + 8 * ch]) = pv[e];
     }
     if (w == 0) {
@@ -434,8 +440,10 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
       // ct >= NIT: U~ columns w*IW + 16(ct-NIT) (kept in U).  Earlier block
       // rows come back as fp16 B operands: W from LDS, U~ from registers.
       f16x4 Wh[3][NIT];  // earlier block rows of W as fp16 operands
-      // transpose-read base of this lane in the K tile at this wave's columns
-      const uint32_t xb = tr_base(lds_addr(sm.k) + 2 * (w * IW + tro));
+      // transpose-read bases of this lane in the K and V tiles at this
+      // wave's columns
+      const uint32_t xk = tr_base(lds_addr(sm.k) + 2 * (w * IW + tro));
+      const uint32_t xv = tr_base(lds_addr(sm.w) + 2 * (w * IW + trv));
       auto yprev = [&](int m, int ct) -> f16x4 {
         if (ct < NIT) return Wh[m][ct];
         return to_f16x4(U[m][ct - NIT]);
@@ -449,9 +457,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
         const f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[16 * bi + 4 * lg]);
 #pragma unroll
         for (int ct = 0; ct < NIT; ++ct) {
-          const int off = 2 * (16 * bi * (D + 8) + 16 * ct);
-          const f16x4 kx = as_f16x4(lds_tr4(xb, off));
-          const u16x4 vx = lds_tr4(xb, off + kVOff);
+          const f16x4 kx = as_f16x4(lds_tr4(xk, 2 * (16 * bi * ChunkSmem<D>::kKS + 16 * ct)));
+          const u16x4 vx = lds_tr4(xv, 2 * (16 * bi * kWS + 16 * ct));
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             X[ct][r] = static_cast<float>(kx[r]) * bg4[r];
@@ -490,21 +497,22 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
           }
         }
       }
-      tr_keep(xb);
+      tr_keep(xk);
+      tr_keep(xv);
       __syncthreads();  // -W complete
     } else {
-      const uint32_t xb = tr_base(lds_addr(sm.k) + 2 * (w * IW + tro));
+      const uint32_t xv = tr_base(lds_addr(sm.w) + 2 * (w * IW + trv));
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[16 * tt + 4 * lg]);
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-          const u16x4 vx = lds_tr4(xb, kVOff + 2 * (16 * tt * (D + 8) + 16 * it));
+          const u16x4 vx = lds_tr4(xv, 2 * (16 * tt * kWS + 16 * it));
 #pragma unroll
           for (int r = 0; r < 4; ++r) U[tt][it][r] = raw_to_f32<TI>(vx[r]) * be4[r];
         }
       }
-      tr_keep(xb);
+      tr_keep(xv);
     }
 
     // ---- U = U~ - W S^T, one key k-step at a time -------------------------
@@ -564,8 +572,8 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int t = 16 * (2 * tp + u) + lr;
-            const f16x8 qb = cat44(lds4(&sm.q[swz<D>(t, 32 * kk + 4 * lg)]),
-                                   lds4(&sm.q[swz<D>(t, 32 * kk + 16 + 4 * lg)]));
+            const f16x8 qb = cat44(lds4(&sm.q[qidx<D>(t, 32 * kk + 4 * lg)]),
+                                   lds4(&sm.q[qidx<D>(t, 32 * kk + 16 + 4 * lg)]));
 #pragma unroll
             for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(s16[it], qb, O[u][it]);
           }
@@ -606,8 +614,9 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           // K^T rows 16jt.., token k-slots {32ks+4lg.., 32ks+16+4lg..}
-          const f16x8 av = cat44(as_f16x4(lds_tr4(sb, 2 * (32 * ks * (D + 8) + 16 * jt))),
-                                 as_f16x4(lds_tr4(sb, 2 * ((32 * ks + 16) * (D + 8) + 16 * jt))));
+          constexpr int KS = ChunkSmem<D>::kKS;
+          const f16x8 av = cat44(as_f16x4(lds_tr4(sb, 2 * (32 * ks * KS + 16 * jt))),
+                                 as_f16x4(lds_tr4(sb, 2 * ((32 * ks + 16) * KS + 16 * jt))));
 #pragma unroll
           for (int it = 0; it < NIT; ++it) S[jt][it] = mfma16x16x32(av, UD[ks][it], S[jt][it]);
         }
