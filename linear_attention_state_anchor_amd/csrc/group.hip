@@ -4,12 +4,12 @@
 // zero initial state per group, the group's final FFN omitted).
 //
 // Per GDN layer (pre-norm residual block without FFN):
-//   r_t  = (mean x_t^2 + eps)^(-1/2)                       rms_rows_kernel
-//   P    = r o (x W_in), packed columns k|v|a|b|pad|q|z    gemm_kernel (MFMA)
+//   xh   = fp16(x / sqrt(mean x^2 + eps))                  rms_norm_kernel
+//   P    = xh W_in (fp16), packed columns k|v|a|b|pad|q|z  gemm_kernel (MFMA)
 //   q,k  = L2norm(SiLU(conv(P_q,P_k))), v = SiLU(conv(P_v)),
-//   z, log a = -softplus(P_a), b = sigmoid(P_b)            frontend_kernel
+//   log a = -softplus(P_a), b = sigmoid(P_b)               frontend_kernel
 //   S, o = gated delta rule from S_0 = 0                   launch_gdn_chunk
-//   y    = rms(o) o SiLU(z) per value head                 gated_norm_kernel
+//   y    = rms(o) o SiLU(P_z) per value head               gated_norm_kernel
 //   x   <- x + y W_out                                     gemm_kernel (MFMA)
 // The last GDN layer of the group only needs its state: its projection
 // covers the k|v|a|b prefix of the packed columns (plus q when the conv
@@ -17,6 +17,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "sr_common.hpp"
@@ -120,243 +121,333 @@ __global__ void pack_wout_kernel(const uint16_t* __restrict__ w, LayerShape L,
 }
 
 // ---------------------------------------------------------------------------
-// row statistics: r_t = (mean_c x_t,c^2 + eps)^(-1/2), one wave per row
+// pre-mixer RMSNorm (unit weight): xh_t = fp16(x_t / sqrt(mean_c x_t,c^2 + eps)),
+// one wave per row, 8 consecutive elements per lane and step
 // ---------------------------------------------------------------------------
 template <typename TX>
-__global__ __launch_bounds__(256) void rms_rows_kernel(const void* __restrict__ x, int rows,
-                                                       int cols, float eps,
-                                                       float* __restrict__ r) {
+__device__ __forceinline__ void load8f(const void* x, size_t idx, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8f<BF16>(const void* x, size_t idx, float (&v)[8]) {
+  const u16x8 b = *reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(x) + idx);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = bf16_to_f32(b[e]);
+}
+template <>
+__device__ __forceinline__ void load8f<F32>(const void* x, size_t idx, float (&v)[8]) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + idx);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + idx + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = lo[e];
+    v[4 + e] = hi[e];
+  }
+}
+
+template <typename TX>
+__global__ __launch_bounds__(256) void rms_norm_kernel(const void* __restrict__ x, int rows, int cols,
+                                                       float eps, _Float16* __restrict__ xh) {
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (row >= rows) return;
+  const size_t base = static_cast<size_t>(row) * cols;
   float s = 0.0f;
-  for (int c = lane; c < cols; c += kWave) {
-    const float v = load1<TX>(x, static_cast<size_t>(row) * cols + c);
-    s = fmaf(v, v, s);
+  for (int c = 8 * lane; c < cols; c += 8 * kWave) {
+    float v[8];
+    load8f<TX>(x, base + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(v[e], v[e], s);
   }
 #pragma unroll
   for (int off = kWave / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
-  if (lane == 0) r[row] = rsqrtf(s / static_cast<float>(cols) + eps);
+  const float r = rsqrtf(s / static_cast<float>(cols) + eps);
+  for (int c = 8 * lane; c < cols; c += 8 * kWave) {
+    float v[8];
+    load8f<TX>(x, base + c, v);
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(v[e] * r);
+    *reinterpret_cast<f16x8*>(xh + base + c) = h;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// C[M][N] = epilogue(A[M][K] . Bt[N][K]^T), fp16 matrix-core operands
-//   EPI_SCALE: C = rs[m] * acc                 (fp32 out)
-//   EPI_RESID: C = X[m][n] + acc, X of type TX (fp32 out; C may alias X)
-// Tile 128 x 128 x 64, 4 waves of 64 x 64, 32x32x16 MFMAs; the next k-tile
-// is prefetched into registers while the current one is in LDS.
-// Requirements: K % 64 == 0, N % 128 == 0, lda/ldb multiples of 8.
+// C[M][N] = A[M][K] . Bt[N][K]^T on the matrix cores: fp16 operands, fp32
+// accumulation.
+//   EPI_STORE16: C fp16 = acc
+//   EPI_RESID:   C fp32 = X[m][n] + acc, X of type TX (C may alias X)
+// Workgroup tile 256 x 256 x 64, 4 waves of 128 x 128 (16 accumulators of
+// 32x32x16 MFMAs each, held in the accumulation registers); LDS is double
+// buffered, the next k-tile is loaded into registers while the current one
+// is multiplied, so each k-tile costs one barrier.  One workgroup per CU.
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, so each XCD is
+// given a contiguous range of a grouped order (8 M-tiles wide, walking N):
+// the ~32 tiles an XCD runs at a time share 8 A and 4 B panels in its L2.
+// Requirements: K % 64 == 0, lda/ldb multiples of 8; M and N are guarded.
 // ---------------------------------------------------------------------------
-constexpr int EPI_SCALE = 0;
+constexpr int EPI_STORE16 = 0;
 constexpr int EPI_RESID = 1;
-constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;
+constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8;
+constexpr int GGROUP = 8;  // M-tiles per group of the tile order
+constexpr int kXcdG = 8;   // XCDs
 
-template <typename TA>
-struct ATile;
-template <>
-struct ATile<BF16> {  // 8 elements per 16-byte load
-  static constexpr int kPer = 8;
-};
-template <>
-struct ATile<F16> {
-  static constexpr int kPer = 8;
-};
-template <>
-struct ATile<F32> {  // 4 elements per 16-byte load
-  static constexpr int kPer = 4;
-};
-
-template <typename TA, int EPI, typename TX>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const void* __restrict__ A, int lda,
+template <int EPI, typename TX>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict__ A, int lda,
                                                       const _Float16* __restrict__ Bt, int ldb,
-                                                      int M, int N, int K, float* C, int ldc,
-                                                      const float* __restrict__ rs,
+                                                      int M, int N, int K, void* C, int ldc,
                                                       const void* X, int ldx) {
-  __shared__ _Float16 sa[GBM * GLD];
-  __shared__ _Float16 sb[GBN * GLD];
-  constexpr int PER = ATile<TA>::kPer;
-  constexpr int A_LOADS = GBM * GBK / PER / 256;  // 16-byte loads per thread
-  constexpr int B_LOADS = GBN * GBK / 8 / 256;
+  __shared__ _Float16 sm[2][2][GBM * GLD];  // [buffer][A | B]
+  constexpr int LOADS = GBM * GBK / 8 / 256;  // 16-byte loads per thread per operand
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l = tid % kWave;
   const int wm = w / 2, wn = w % 2;
-  // tiles: blockIdx.x over N (fast), blockIdx.y over M
-  const int n0 = blockIdx.x * GBN;
-  const int m0 = blockIdx.y * GBM;
+  int tm, tn;
+  {
+    const int n_m = (M + GBM - 1) / GBM, n_n = (N + GBN - 1) / GBN;
+    const int tiles = n_m * n_n, per_xcd = (tiles + kXcdG - 1) / kXcdG;
+    const int q = (blockIdx.x % kXcdG) * per_xcd + blockIdx.x / kXcdG;
+    if (q >= tiles) return;
+    const int group = q / (GGROUP * n_n), first = group * GGROUP;
+    const int gsz = min(n_m - first, GGROUP);
+    tm = first + (q % (GGROUP * n_n)) % gsz;
+    tn = (q % (GGROUP * n_n)) / gsz;
+  }
+  const int n0 = tn * GBN;
+  const int m0 = tm * GBM;
 
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 ra[A_LOADS], rb[B_LOADS];
-  auto load_tiles = [&](int k0) {
+  // Thread tid moves the 16-byte pieces (row tid/8 + 32e, chunk tid%8), e <
+  // LOADS, of each operand tile.  Rows past M (N) are clamped to the last
+  // row: they are computed and never stored, and the loop stays branch-free.
+  // Byte offsets fit in 32 bits (the launcher splits larger problems), so a
+  // load is one instruction: uniform base (k0) + per-thread offset.
+  uint32_t aoff[LOADS], boff[LOADS];
 #pragma unroll
-    for (int e = 0; e < A_LOADS; ++e) {
-      const int item = tid + 256 * e;
-      const int row = item / (GBK / PER), ch = item % (GBK / PER);
-      const int m = m0 + row;
-      ra[e] = u32x4{0u, 0u, 0u, 0u};
-      if (m < M) {
-        const char* p = static_cast<const char*>(A) +
-                        (static_cast<size_t>(m) * lda + k0 + ch * PER) * sizeof(uint16_t) *
-                            (PER == 4 ? 2 : 1);
-        ra[e] = *reinterpret_cast<const u32x4*>(p);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < B_LOADS; ++e) {
-      const int item = tid + 256 * e;
-      const int row = item / (GBK / 8), ch = item % (GBK / 8);
-      rb[e] = *reinterpret_cast<const u32x4*>(Bt + static_cast<size_t>(n0 + row) * ldb + k0 + ch * 8);
-    }
+  for (int e = 0; e < LOADS; ++e) {
+    const int row = tid / (GBK / 8) + (256 / (GBK / 8)) * e, ch = tid % (GBK / 8);
+    aoff[e] = static_cast<uint32_t>((static_cast<size_t>(min(m0 + row, M - 1)) * lda + 8 * ch) * 2);
+    boff[e] = static_cast<uint32_t>((static_cast<size_t>(min(n0 + row, N - 1)) * ldb + 8 * ch) * 2);
+  }
+  u32x4 ra[LOADS], rb[LOADS];
+  auto gload_a = [&](int k0, int e) {
+    ra[e] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A + k0) + aoff[e]);
   };
-  auto store_tiles = [&]() {
-#pragma unroll
-    for (int e = 0; e < A_LOADS; ++e) {
-      const int item = tid + 256 * e;
-      const int row = item / (GBK / PER), ch = item % (GBK / PER);
-      if (PER == 8) {
-        f16x8 v;
-        if (std::is_same<TA, F16>::value) {
-          v = __builtin_bit_cast(f16x8, ra[e]);
-        } else {
-          const u16x8 b = __builtin_bit_cast(u16x8, ra[e]);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) v[x] = static_cast<_Float16>(bf16_to_f32(b[x]));
-        }
-        *reinterpret_cast<f16x8*>(&sa[row * GLD + ch * 8]) = v;
-      } else {
-        const f32x4 f = __builtin_bit_cast(f32x4, ra[e]);
-        *reinterpret_cast<f16x4*>(&sa[row * GLD + ch * 4]) = to_f16x4(f);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < B_LOADS; ++e) {
-      const int item = tid + 256 * e;
-      const int row = item / (GBK / 8), ch = item % (GBK / 8);
-      *reinterpret_cast<u32x4*>(&sb[row * GLD + ch * 8]) = rb[e];
-    }
+  auto gload_b = [&](int k0, int e) {
+    rb[e] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(Bt + k0) + boff[e]);
+  };
+  auto store_tile = [&](int buf, int e) {
+    const int row = tid / (GBK / 8) + (256 / (GBK / 8)) * e, ch = tid % (GBK / 8);
+    *reinterpret_cast<u32x4*>(&sm[buf][0][row * GLD + 8 * ch]) = ra[e];
+    *reinterpret_cast<u32x4*>(&sm[buf][1][row * GLD + 8 * ch]) = rb[e];
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  load_tiles(0);
-  for (int k0 = 0; k0 < K; k0 += GBK) {
-    __syncthreads();
-    store_tiles();
-    __syncthreads();
-    if (k0 + GBK < K) load_tiles(k0 + GBK);
+  // lane l reads rows/columns l % 32 of each 32-wide fragment, k 8(l/32)..+7
+  f16x8 av[2][4], bv[2][4];
+  auto load_frag = [&](int buf, int ks, f16x8(&fa)[4], f16x8(&fb)[4]) {
 #pragma unroll
-    for (int ks = 0; ks < GBK / 16; ++ks) {
-      f16x8 av[2], bv[2];
+    for (int i = 0; i < 4; ++i)
+      fa[i] = *reinterpret_cast<const f16x8*>(&sm[buf][0][(wm * 128 + 32 * i + l % 32) * GLD + 16 * ks + 8 * (l / 32)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        av[i] = *reinterpret_cast<const f16x8*>(
-            &sa[(wm * 64 + 32 * i + l % 32) * GLD + ks * 16 + 8 * (l / 32)]);
+    for (int j = 0; j < 4; ++j)
+      fb[j] = *reinterpret_cast<const f16x8*>(&sm[buf][1][(wn * 128 + 32 * j + l % 32) * GLD + 16 * ks + 8 * (l / 32)]);
+  };
+  auto mma = [&](int h) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bv[j] = *reinterpret_cast<const f16x8*>(
-            &sb[(wn * 64 + 32 * j + l % 32) * GLD + ks * 16 + 8 * (l / 32)]);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(av[h][i], bv[h][j], acc[i][j]);
+  };
+
+  const int nk = K / GBK;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+  for (int e = 0; e < LOADS; ++e) {
+    gload_a(0, e);
+    gload_b(0, e);
+  }
+#pragma unroll
+  for (int e = 0; e < LOADS; ++e) store_tile(0, e);
+  __syncthreads();
+  // Per k-tile: four k16 steps of 16 MFMAs.  Interleaved with them: the next
+  // step's fragment reads, the next k-tile's global loads (A in step 0, B in
+  // step 1) and its LDS stores (step 3, into the other buffer).  The last
+  // k-tile reloads itself, so the body has no branches.
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const int kn = (kt + 1 < nk ? kt + 1 : kt) * GBK;
+    load_frag(buf, 0, av[0], bv[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 0
+    load_frag(buf, 1, av[1], bv[1]);
+#pragma unroll
+    for (int e = 0; e < LOADS; ++e) gload_a(kn, e);
+    mma(0);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1
+    load_frag(buf, 2, av[0], bv[0]);
+#pragma unroll
+    for (int e = 0; e < LOADS; ++e) gload_b(kn, e);
+    mma(1);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // step 2
+    load_frag(buf, 3, av[1], bv[1]);
+    mma(0);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // step 3
+#pragma unroll
+    for (int e = 0; e < LOADS; ++e) store_tile(buf ^ 1, e);
+    mma(1);
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
   }
   // epilogue: lane holds column l%32 and rows 8(r/4) + 4(l/32) + r%4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 128 + 32 * j + l % 32;
+      if (n >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + 32 * i + 8 * (r / 4) + 4 * (l / 32) + (r % 4);
-        const int n = n0 + wn * 64 + 32 * j + l % 32;
-        if (m >= M || n >= N) continue;
+        const int m = m0 + wm * 128 + 32 * i + 8 * (r / 4) + 4 * (l / 32) + (r % 4);
+        if (m >= M) continue;
         const size_t ci = static_cast<size_t>(m) * ldc + n;
-        if (EPI == EPI_SCALE) {
-          C[ci] = rs[m] * acc[i][j][r];
-        } else {
-          C[ci] = load1<TX>(X, static_cast<size_t>(m) * ldx + n) + acc[i][j][r];
-        }
+        if (EPI == EPI_STORE16)
+          static_cast<_Float16*>(C)[ci] = static_cast<_Float16>(acc[i][j][r]);
+        else
+          static_cast<float*>(C)[ci] =
+              load1<TX>(X, static_cast<size_t>(m) * ldx + n) + acc[i][j][r];
       }
+    }
 }
 
 // ---------------------------------------------------------------------------
-// front-end epilogue, one workgroup per token, one wave per 128-channel head:
-// causal conv (zero history before the sequence start) + SiLU on q|k|v,
-// per-head L2 norm of q and k, z copy, gates.
+// front end: one workgroup per 64-token block and head (grid y): causal
+// depthwise conv over the projection rows (zero history before each token's
+// sequence start) + SiLU on the k, v and q heads, per-head L2 norm of q and
+// k; the last y index does the gates of the block.  A wave walks 16 tokens
+// with a sliding window of the last `width` rows in registers; a lane owns
+// D/64 adjacent channels, so every row access is one coalesced 256-byte (or
+// 128-byte) wave load.  z is not copied: the gated RMSNorm reads it from P.
 // ---------------------------------------------------------------------------
+constexpr int FT = 64;   // tokens per workgroup
+constexpr int MAXW = 8;  // largest supported conv width
+
+template <int D>
 __global__ __launch_bounds__(256) void frontend_kernel(
-    const float* __restrict__ P, int ldp, LayerShape L, const float* __restrict__ convw,
-    const int32_t* __restrict__ seq_start, int T, float l2_eps, bool last,
+    const _Float16* __restrict__ P, int ldp, LayerShape L, const float* __restrict__ convw,
+    const int32_t* __restrict__ seq_start, int T, float l2_eps, int n_conv_heads,
     _Float16* __restrict__ qo, _Float16* __restrict__ ko, _Float16* __restrict__ vo,
-    _Float16* __restrict__ zo, float* __restrict__ la, float* __restrict__ be) {
-  const int t = blockIdx.x;
-  if (t >= T) return;
-  const int s0 = seq_start[t];
-  const int d = L.d;
-  const int W = L.width;
-  // heads: k (h_k), v (h_v), q (h_k, not for the last layer), z (h_v), gates
-  const int nk = L.h_k, nv = L.h_v;
-  const int n_heads = last ? nk + nv : 2 * nk + 2 * nv;
-  const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  for (int hh = wv; hh < n_heads; hh += blockDim.x / kWave) {
-    int pc0, kind;  // kind 0: k, 1: v, 2: q, 3: z
-    int hidx;
-    if (hh < nk) { kind = 0; hidx = hh; pc0 = hh * d; }
-    else if (hh < nk + nv) { kind = 1; hidx = hh - nk; pc0 = nk * d + hidx * d; }
-    else if (hh < 2 * nk + nv) { kind = 2; hidx = hh - nk - nv; pc0 = L.q_off() + hidx * d; }
-    else { kind = 3; hidx = hh - 2 * nk - nv; pc0 = L.z_off() + hidx * d; }
-    float vals[4];
-    int nvals = 0;
-    float ss = 0.0f;
-    for (int c = lane; c < d; c += kWave) {
-      const int pc = pc0 + c;
-      float y;
-      if (kind == 3) {
-        y = P[static_cast<size_t>(t) * ldp + pc];
-      } else {
-        const int ch = conv_channel(L, pc);
-        float acc = 0.0f;
-        for (int j = 0; j < W; ++j) {
-          const int tt = t - (W - 1) + j;
-          if (tt >= s0) acc = fmaf(convw[ch * W + j], P[static_cast<size_t>(tt) * ldp + pc], acc);
-        }
-        y = acc / (1.0f + __expf(-acc));  // SiLU
-      }
-      vals[nvals++] = y;
-      ss = fmaf(y, y, ss);
+    float* __restrict__ la, float* __restrict__ be) {
+  constexpr int CPL = D / kWave;  // channels per lane
+  const int t0 = blockIdx.x * FT;
+  const int hh = blockIdx.y;
+  const int nk = L.h_k, nv = L.h_v, W = L.width;
+  if (hh == n_conv_heads) {  // gates
+    for (int e = threadIdx.x; e < FT * nv; e += blockDim.x) {
+      const int t = t0 + e / nv, h = e % nv;
+      if (t >= T) break;
+      const size_t pr = static_cast<size_t>(t) * ldp;
+      la[static_cast<size_t>(t) * nv + h] = -softplus(static_cast<float>(P[pr + L.a_off() + h]));
+      be[static_cast<size_t>(t) * nv + h] = sigmoid(static_cast<float>(P[pr + L.b_off() + h]));
     }
-    if (kind == 0 || kind == 2) {
+    return;
+  }
+  int kind, hidx, pc0, nh;  // kind 0: k, 1: v, 2: q
+  _Float16* out;
+  if (hh < nk) {
+    kind = 0; hidx = hh; pc0 = hh * D; nh = nk; out = ko;
+  } else if (hh < nk + nv) {
+    kind = 1; hidx = hh - nk; pc0 = nk * D + hidx * D; nh = nv; out = vo;
+  } else {
+    kind = 2; hidx = hh - nk - nv; pc0 = L.q_off() + hidx * D; nh = nk; out = qo;
+  }
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int c0 = CPL * lane;
+  const int ch0 = conv_channel(L, pc0 + c0);  // conv channels ch0 .. ch0+CPL-1
+  float wt[CPL][MAXW];  // wt[e][k]: tap applied to row t-k
+#pragma unroll
+  for (int e = 0; e < CPL; ++e)
+#pragma unroll
+    for (int k = 0; k < MAXW; ++k) wt[e][k] = k < W ? convw[(ch0 + e) * W + (W - 1 - k)] : 0.0f;
+  // win[MAXW-1-k] holds row t-k of this lane's channels
+  float win[MAXW][CPL];
+#pragma unroll
+  for (int j = 0; j < MAXW; ++j)
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) win[j][e] = 0.0f;
+  const int tb = t0 + 16 * wv;
+  auto push = [&](int row) {
+#pragma unroll
+    for (int j = 0; j < MAXW - 1; ++j)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) win[j][e] = win[j + 1][e];
+    const _Float16* pr = P + static_cast<size_t>(row) * ldp + pc0 + c0;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) win[MAXW - 1][e] = (row >= 0 && row < T) ? static_cast<float>(pr[e]) : 0.0f;
+  };
+  for (int row = tb - (W - 1); row < tb; ++row) push(row);
+  for (int i = 0; i < 16; ++i) {
+    const int t = tb + i;
+    if (t >= T) break;
+    push(t);
+    const int back = t - seq_start[t];  // rows t-back .. t belong to t's sequence
+    float y[CPL];
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < MAXW; ++k)
+        if (k <= back) acc = fmaf(wt[e][k], win[MAXW - 1 - k][e], acc);
+      y[e] = acc / (1.0f + __expf(-acc));  // SiLU
+      ss = fmaf(y[e], y[e], ss);
+    }
+    if (kind != 1) {
 #pragma unroll
       for (int off = kWave / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
       const float inv = rsqrtf(ss + l2_eps);
-      for (int e = 0; e < nvals; ++e) vals[e] *= inv;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) y[e] *= inv;
     }
-    _Float16* out = kind == 0 ? ko + (static_cast<size_t>(t) * nk + hidx) * d
-                  : kind == 1 ? vo + (static_cast<size_t>(t) * nv + hidx) * d
-                  : kind == 2 ? qo + (static_cast<size_t>(t) * nk + hidx) * d
-                              : zo + (static_cast<size_t>(t) * nv + hidx) * d;
-    int e = 0;
-    for (int c = lane; c < d; c += kWave) out[c] = static_cast<_Float16>(vals[e++]);
-  }
-  // gates
-  for (int h = threadIdx.x; h < nv; h += blockDim.x) {
-    const float av = P[static_cast<size_t>(t) * ldp + L.a_off() + h];
-    const float bv = P[static_cast<size_t>(t) * ldp + L.b_off() + h];
-    la[static_cast<size_t>(t) * nv + h] = -softplus(av);
-    be[static_cast<size_t>(t) * nv + h] = sigmoid(bv);
+    _Float16* o = out + (static_cast<size_t>(t) * nh + hidx) * D + c0;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) o[e] = static_cast<_Float16>(y[e]);
   }
 }
 
 // conv state: last W-1 pre-conv rows of q|k|v per sequence (original
 // channel order), oldest first, zero where the sequence is shorter
-__global__ void conv_state_kernel(const float* __restrict__ P, int ldp, LayerShape L,
+__global__ void conv_state_kernel(const _Float16* __restrict__ P, int ldp, LayerShape L,
                                   const int32_t* __restrict__ cu, int n_seqs,
                                   float* __restrict__ out) {
   const int n = blockIdx.y;
@@ -367,7 +458,7 @@ __global__ void conv_state_kernel(const float* __restrict__ P, int ldp, LayerSha
     const int start = cu[n], end = cu[n + 1];
     const int pos = end - W1 + j;
     float v = 0.0f;
-    if (pos >= start) v = P[static_cast<size_t>(pos) * ldp + L.packed_col(c)];
+    if (pos >= start) v = static_cast<float>(P[static_cast<size_t>(pos) * ldp + L.packed_col(c)]);
     out[(static_cast<size_t>(n) * cd + c) * W1 + j] = v;
   }
 }
@@ -392,15 +483,17 @@ __global__ void seq_start_kernel(const int32_t* __restrict__ cu, int n_seqs, int
   out[t] = cu[lo];
 }
 
-// y = o / sqrt(mean(o^2) + eps) * SiLU(z), per (token, value head), fp16 out
+// y = o / sqrt(mean(o^2) + eps) * SiLU(z), per (token, value head), fp16 out;
+// z is read from the projection rows (columns z_off + head * d)
 __global__ __launch_bounds__(256) void gated_norm_kernel(const _Float16* __restrict__ o,
-                                                         const _Float16* __restrict__ z,
-                                                         int rows, int d, float eps,
-                                                         _Float16* __restrict__ y) {
+                                                         const _Float16* __restrict__ P, int ldp,
+                                                         int z_off, int h_v, int rows, int d,
+                                                         float eps, _Float16* __restrict__ y) {
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;  // (token, head) row
   const int lane = threadIdx.x % kWave;
   if (row >= rows) return;
   const size_t base = static_cast<size_t>(row) * d;
+  const _Float16* z = P + static_cast<size_t>(row / h_v) * ldp + z_off + (row % h_v) * d;
   float ss = 0.0f;
   for (int c = lane; c < d; c += kWave) {
     const float v = static_cast<float>(o[base + c]);
@@ -410,7 +503,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(const _Float16* __restr
   for (int off = kWave / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
   const float inv = rsqrtf(ss / static_cast<float>(d) + eps);
   for (int c = lane; c < d; c += kWave) {
-    const float zv = static_cast<float>(z[base + c]);
+    const float zv = static_cast<float>(z[c]);
     y[base + c] = static_cast<_Float16>(static_cast<float>(o[base + c]) * inv * silu(zv));
   }
 }
@@ -419,7 +512,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(const _Float16* __restr
 // workspace layout of one group call
 // ---------------------------------------------------------------------------
 struct Workspace {
-  size_t xres, rs, p, q, k, v, z, la, be, o, y, ss, total;
+  size_t xres, xh, p, q, k, v, la, be, o, y, ss, total;
 };
 
 Workspace plan(const LayerShape& L, int T) {
@@ -432,12 +525,11 @@ Workspace plan(const LayerShape& L, int T) {
   };
   const size_t t = static_cast<size_t>(T);
   w.xres = take(t * L.hidden * 4);
-  w.rs = take(t * 4);
-  w.p = take(t * L.n_all() * 4);
+  w.xh = take(t * L.hidden * 2);
+  w.p = take(t * L.n_all() * 2);
   w.q = take(t * L.h_k * L.d * 2);
   w.k = take(t * L.h_k * L.d * 2);
   w.v = take(t * L.h_v * L.d * 2);
-  w.z = take(t * L.h_v * L.d * 2);
   w.la = take(t * L.h_v * 4);
   w.be = take(t * L.h_v * 4);
   w.o = take(t * L.h_v * L.d * 2);
@@ -447,14 +539,31 @@ Workspace plan(const LayerShape& L, int T) {
   return w;
 }
 
-template <typename TA, int EPI, typename TX>
-hipError_t gemm(const void* A, int lda, const _Float16* Bt, int ldb, int M, int N, int K,
-                float* C, int ldc, const float* rs, const void* X, int ldx, hipStream_t s) {
-  if (M == 0) return hipSuccess;
-  dim3 grid(N / GBN, (M + GBM - 1) / GBM), block(256);
-  hipLaunchKernelGGL((gemm_kernel<TA, EPI, TX>), grid, block, 0, s, A, lda, Bt, ldb, M, N, K, C,
-                     ldc, rs, X, ldx);
-  return hipGetLastError();
+template <int EPI, typename TX>
+hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, int N, int K,
+                void* C, int ldc, const void* X, int ldx, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  // the kernel addresses A and Bt with 32-bit byte offsets: split M so that
+  // every launch stays below 2^31 bytes of A
+  const size_t row_bytes = static_cast<size_t>(lda) * 2;
+  const int mc = static_cast<int>(std::max<size_t>(GBM, ((size_t{1} << 31) / row_bytes) / GBM * GBM));
+  for (int m_at = 0; m_at < M; m_at += mc) {
+    const int mm = std::min(mc, M - m_at);
+    const int tiles = ((N + GBN - 1) / GBN) * ((mm + GBM - 1) / GBM);
+    dim3 grid((tiles + kXcdG - 1) / kXcdG * kXcdG), block(256);
+    void* Cm = EPI == EPI_STORE16
+                   ? static_cast<void*>(static_cast<_Float16*>(C) + static_cast<size_t>(m_at) * ldc)
+                   : static_cast<void*>(static_cast<float*>(C) + static_cast<size_t>(m_at) * ldc);
+    const void* Xm = X == nullptr ? nullptr
+                     : std::is_same<TX, F32>::value
+                         ? static_cast<const void*>(static_cast<const float*>(X) + static_cast<size_t>(m_at) * ldx)
+                         : static_cast<const void*>(static_cast<const uint16_t*>(X) + static_cast<size_t>(m_at) * ldx);
+    hipLaunchKernelGGL((gemm_kernel<EPI, TX>), grid, block, 0, s, A + static_cast<size_t>(m_at) * lda,
+                       lda, Bt, ldb, mm, N, K, Cm, ldc, Xm, ldx);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 bool shape_ok(const sr_group_desc* d) {
@@ -539,12 +648,11 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   float* xres = reinterpret_cast<float*>(ws + W.xres);
-  float* rs = reinterpret_cast<float*>(ws + W.rs);
-  float* P = reinterpret_cast<float*>(ws + W.p);
+  _Float16* xh = reinterpret_cast<_Float16*>(ws + W.xh);
+  _Float16* P = reinterpret_cast<_Float16*>(ws + W.p);
   _Float16* qb = reinterpret_cast<_Float16*>(ws + W.q);
   _Float16* kb = reinterpret_cast<_Float16*>(ws + W.k);
   _Float16* vb = reinterpret_cast<_Float16*>(ws + W.v);
-  _Float16* zb = reinterpret_cast<_Float16*>(ws + W.z);
   float* la = reinterpret_cast<float*>(ws + W.la);
   float* be = reinterpret_cast<float*>(ws + W.be);
   _Float16* ob = reinterpret_cast<_Float16*>(ws + W.o);
@@ -566,29 +674,33 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
     const _Float16* wout = reinterpret_cast<const _Float16*>(pk + L.win_bytes() + L.conv_bytes());
     float* st = states + state_stride * li;
     if (T > 0) {
-      // x of this layer: the anchors (bf16) for the first, the residual after
+      // x of this layer: the anchors (bf16) for the first, the residual after;
+      // xh = RMSNorm(x) in fp16, the A operand of the projection
       const bool from_anchors = li == 0;
       if (from_anchors)
-        hipLaunchKernelGGL(sr::rms_rows_kernel<sr::BF16>, dim3((T + 3) / 4), dim3(256), 0, s,
-                           anchors, T, d->hidden, d->rms_eps, rs);
+        hipLaunchKernelGGL(sr::rms_norm_kernel<sr::BF16>, dim3((T + 3) / 4), dim3(256), 0, s,
+                           anchors, T, d->hidden, d->rms_eps, xh);
       else
-        hipLaunchKernelGGL(sr::rms_rows_kernel<sr::F32>, dim3((T + 3) / 4), dim3(256), 0, s,
-                           static_cast<const void*>(xres), T, d->hidden, d->rms_eps, rs);
+        hipLaunchKernelGGL(sr::rms_norm_kernel<sr::F32>, dim3((T + 3) / 4), dim3(256), 0, s,
+                           static_cast<const void*>(xres), T, d->hidden, d->rms_eps, xh);
       if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
       // the last layer needs k|v|a|b for its state, and q as well when its
       // conv window is returned (q follows the state prefix in the packing)
       const int N = !is_last ? L.n_all()
                   : conv_states ? static_cast<int>(sr::align_up(L.q_off() + d->h_k * d->d, 128))
                                 : L.n_state_pad();
-      hipError_t e =
-          from_anchors
-              ? sr::gemm<sr::BF16, sr::EPI_SCALE, sr::F32>(anchors, d->hidden, win, d->hidden, T, N,
-                                                          d->hidden, P, L.n_all(), rs, nullptr, 0, s)
-              : sr::gemm<sr::F32, sr::EPI_SCALE, sr::F32>(xres, d->hidden, win, d->hidden, T, N,
-                                                         d->hidden, P, L.n_all(), rs, nullptr, 0, s);
-      if (e != hipSuccess) return SR_ELAUNCH;
-      hipLaunchKernelGGL(sr::frontend_kernel, dim3(T), dim3(256), 0, s, P, L.n_all(), L, convw, sst,
-                         T, d->l2_eps, is_last, qb, kb, vb, zb, la, be);
+      if (sr::gemm<sr::EPI_STORE16, sr::F32>(xh, d->hidden, win, d->hidden, T, N, d->hidden, P,
+                                             L.n_all(), nullptr, 0, s) != hipSuccess)
+        return SR_ELAUNCH;
+      // conv heads: k, v (and q unless this is the last layer), then gates
+      const int n_conv = is_last ? d->h_k + d->h_v : 2 * d->h_k + d->h_v;
+      const dim3 fgrid((T + sr::FT - 1) / sr::FT, n_conv + 1);
+      if (d->d == 128)
+        hipLaunchKernelGGL(sr::frontend_kernel<128>, fgrid, dim3(256), 0, s, P, L.n_all(), L, convw,
+                           sst, T, d->l2_eps, n_conv, qb, kb, vb, la, be);
+      else
+        hipLaunchKernelGGL(sr::frontend_kernel<64>, fgrid, dim3(256), 0, s, P, L.n_all(), L, convw,
+                           sst, T, d->l2_eps, n_conv, qb, kb, vb, la, be);
       if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
       if (conv_states) {
         hipLaunchKernelGGL(sr::conv_state_kernel, dim3(64, d->n_seqs), dim3(256), 0, s, P, L.n_all(),
@@ -626,16 +738,14 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
     if (sr::launch_gdn_chunk(g, s) != hipSuccess) return SR_ELAUNCH;
     if (is_last || T == 0) continue;
     const int rows = T * d->h_v;
-    hipLaunchKernelGGL(sr::gated_norm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, ob, zb, rows,
-                       d->d, d->rms_eps, yb);
+    hipLaunchKernelGGL(sr::gated_norm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, ob, P,
+                       L.n_all(), L.z_off(), d->h_v, rows, d->d, d->rms_eps, yb);
     if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
     const int K2 = d->h_v * d->d;
-    hipError_t e = li == 0 ? sr::gemm<sr::F16, sr::EPI_RESID, sr::BF16>(
-                                 yb, K2, wout, K2, T, d->hidden, K2, xres, d->hidden, nullptr,
-                                 anchors, d->hidden, s)
-                           : sr::gemm<sr::F16, sr::EPI_RESID, sr::F32>(
-                                 yb, K2, wout, K2, T, d->hidden, K2, xres, d->hidden, nullptr,
-                                 xres, d->hidden, s);
+    hipError_t e = li == 0 ? sr::gemm<sr::EPI_RESID, sr::BF16>(yb, K2, wout, K2, T, d->hidden, K2,
+                                                               xres, d->hidden, anchors, d->hidden, s)
+                           : sr::gemm<sr::EPI_RESID, sr::F32>(yb, K2, wout, K2, T, d->hidden, K2,
+                                                              xres, d->hidden, xres, d->hidden, s);
     if (e != hipSuccess) return SR_ELAUNCH;
   }
   return SR_OK;
