@@ -120,22 +120,6 @@ __device__ __forceinline__ f32x4 mfma16x16x16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
-// row broadcasts (no LDS round trips).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
-}
-__device__ __forceinline__ float wave_inclusive_sum(float x) {
-  x += dpp_f32<0x111, 0xf>(x);  // row_shr:1
-  x += dpp_f32<0x112, 0xf>(x);  // row_shr:2
-  x += dpp_f32<0x114, 0xf>(x);  // row_shr:4
-  x += dpp_f32<0x118, 0xf>(x);  // row_shr:8
-  x += dpp_f32<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
-  x += dpp_f32<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
-  return x;
-}
-
 // Keeps the scheduler from hoisting the loads of later unrolled iterations
 // above this point (which would make their registers live all at once).
 #define SR_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)

@@ -10,7 +10,7 @@
 //   log a = -softplus(P_a), b = sigmoid(P_b)               frontend_kernel
 //   S, o = gated delta rule from S_0 = 0                   launch_gdn_chunk
 //   y    = rms(o) o SiLU(P_z) per value head               gated_norm_kernel
-//   x   <- x + y W_out                                     gemm_kernel (MFMA)
+//   D    = y W_out (fp32); x <- x + D in the next RMSNorm   gemm_kernel (MFMA)
 // The last GDN layer of the group only needs its state: its projection
 // covers the k|v|a|b prefix of the packed columns (plus q when the conv
 // windows are returned) and no output is formed.
@@ -143,30 +143,45 @@ __device__ __forceinline__ void load8f<F32>(const void* x, size_t idx, float (&v
   }
 }
 
-template <typename TX>
-__global__ __launch_bounds__(256) void rms_norm_kernel(const void* __restrict__ x, int rows, int cols,
-                                                       float eps, _Float16* __restrict__ xh) {
+// ADD: the row is x + D (D fp32: the previous layer's output projection),
+// and the sum is also written back to xres (the fp32 residual stream; it
+// may alias x).
+template <typename TX, bool ADD>
+__global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, const float* __restrict__ dlt,
+                                                       int rows, int cols, float eps,
+                                                       float* xres, _Float16* __restrict__ xh) {
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (row >= rows) return;
   const size_t base = static_cast<size_t>(row) * cols;
+  auto load = [&](int c, float (&v)[8]) {
+    load8f<TX>(x, base + c, v);
+    if (ADD) {
+      float dv[8];
+      load8f<F32>(dlt, base + c, dv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += dv[e];
+    }
+  };
   float s = 0.0f;
   for (int c = 8 * lane; c < cols; c += 8 * kWave) {
     float v[8];
-    load8f<TX>(x, base + c, v);
+    load(c, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf(v[e], v[e], s);
   }
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, kWave);
-  const float r = rsqrtf(s / static_cast<float>(cols) + eps);
+  const float r = rsqrtf(wave_sum(s) / static_cast<float>(cols) + eps);
   for (int c = 8 * lane; c < cols; c += 8 * kWave) {
     float v[8];
-    load8f<TX>(x, base + c, v);
+    load(c, v);
     f16x8 h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(v[e] * r);
     *reinterpret_cast<f16x8*>(xh + base + c) = h;
+    if (ADD) {
+      *reinterpret_cast<f32x4*>(xres + base + c) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(xres + base + c + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
   }
 }
 
@@ -174,7 +189,7 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const void* __restrict__ 
 // C[M][N] = A[M][K] . Bt[N][K]^T on the matrix cores: fp16 operands, fp32
 // accumulation.
 //   EPI_STORE16: C fp16 = acc
-//   EPI_RESID:   C fp32 = X[m][n] + acc, X of type TX (C may alias X)
+//   EPI_STORE32: C fp32 = acc
 // Workgroup tile 256 x 256 x 64, 4 waves of 128 x 128 (16 accumulators of
 // 32x32x16 MFMAs each, held in the accumulation registers); LDS is double
 // buffered, the next k-tile is loaded into registers while the current one
@@ -185,16 +200,15 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const void* __restrict__ 
 // Requirements: K % 64 == 0, lda/ldb multiples of 8; M and N are guarded.
 // ---------------------------------------------------------------------------
 constexpr int EPI_STORE16 = 0;
-constexpr int EPI_RESID = 1;
+constexpr int EPI_STORE32 = 1;
 constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8;
 constexpr int GGROUP = 8;  // M-tiles per group of the tile order
 constexpr int kXcdG = 8;   // XCDs
 
-template <int EPI, typename TX>
+template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict__ A, int lda,
                                                       const _Float16* __restrict__ Bt, int ldb,
-                                                      int M, int N, int K, void* C, int ldc,
-                                                      const void* X, int ldx) {
+                                                      int M, int N, int K, void* C, int ldc) {
   __shared__ _Float16 sm[2][2][GBM * GLD];  // [buffer][A | B]
   constexpr int LOADS = GBM * GBK / 8 / 256;  // 16-byte loads per thread per operand
   const int tid = threadIdx.x;
@@ -344,8 +358,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
         if (EPI == EPI_STORE16)
           static_cast<_Float16*>(C)[ci] = static_cast<_Float16>(acc[i][j][r]);
         else
-          static_cast<float*>(C)[ci] =
-              load1<TX>(X, static_cast<size_t>(m) * ldx + n) + acc[i][j][r];
+          static_cast<float*>(C)[ci] = acc[i][j][r];
       }
     }
 }
@@ -399,49 +412,46 @@ __global__ __launch_bounds__(256) void frontend_kernel(
   for (int e = 0; e < CPL; ++e)
 #pragma unroll
     for (int k = 0; k < MAXW; ++k) wt[e][k] = k < W ? convw[(ch0 + e) * W + (W - 1 - k)] : 0.0f;
-  // win[MAXW-1-k] holds row t-k of this lane's channels
-  float win[MAXW][CPL];
-#pragma unroll
-  for (int j = 0; j < MAXW; ++j)
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) win[j][e] = 0.0f;
+  // all input rows of this wave's 16 tokens are loaded up front (rows
+  // tb-MAXW+1 .. tb+15; those before the window or outside [0, T) read 0)
   const int tb = t0 + 16 * wv;
-  auto push = [&](int row) {
+  constexpr int NR = 16 + MAXW - 1;
+  typedef _Float16 h2 __attribute__((ext_vector_type(CPL)));
+  h2 u[NR];
 #pragma unroll
-    for (int j = 0; j < MAXW - 1; ++j)
+  for (int r = 0; r < NR; ++r) {
+    const int row = tb - (MAXW - 1) + r;
+    const bool ok = row >= 0 && row < T && r >= MAXW - W;
+    u[r] = ok ? *reinterpret_cast<const h2*>(P + static_cast<size_t>(row) * ldp + pc0 + c0) : h2{};
+  }
+  // sequence starts of the wave's 16 tokens, one per lane (broadcast below)
+  const int sq = seq_start[min(tb + lane % 16, T - 1)];
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) win[j][e] = win[j + 1][e];
-    const _Float16* pr = P + static_cast<size_t>(row) * ldp + pc0 + c0;
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) win[MAXW - 1][e] = (row >= 0 && row < T) ? static_cast<float>(pr[e]) : 0.0f;
-  };
-  for (int row = tb - (W - 1); row < tb; ++row) push(row);
   for (int i = 0; i < 16; ++i) {
     const int t = tb + i;
-    if (t >= T) break;
-    push(t);
-    const int back = t - seq_start[t];  // rows t-back .. t belong to t's sequence
+    const int back = t < T ? t - __builtin_amdgcn_readlane(sq, i) : -1;  // rows t-back .. t: t's sequence
     float y[CPL];
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       float acc = 0.0f;
 #pragma unroll
-      for (int k = 0; k < MAXW; ++k)
-        if (k <= back) acc = fmaf(wt[e][k], win[MAXW - 1 - k][e], acc);
+      for (int k = 0; k < MAXW; ++k)  // row t-k is u[MAXW-1+i-k]
+        if (k <= back) acc = fmaf(wt[e][k], static_cast<float>(u[MAXW - 1 + i - k][e]), acc);
       y[e] = acc / (1.0f + __expf(-acc));  // SiLU
       ss = fmaf(y[e], y[e], ss);
     }
     if (kind != 1) {
-#pragma unroll
-      for (int off = kWave / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-      const float inv = rsqrtf(ss + l2_eps);
+      const float inv = rsqrtf(wave_sum(ss) + l2_eps);
 #pragma unroll
       for (int e = 0; e < CPL; ++e) y[e] *= inv;
     }
-    _Float16* o = out + (static_cast<size_t>(t) * nh + hidx) * D + c0;
+    if (t < T) {
+      h2 o;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) o[e] = static_cast<_Float16>(y[e]);
+      for (int e = 0; e < CPL; ++e) o[e] = static_cast<_Float16>(y[e]);
+      *reinterpret_cast<h2*>(out + (static_cast<size_t>(t) * nh + hidx) * D + c0) = o;
+    }
   }
 }
 
@@ -484,27 +494,37 @@ __global__ void seq_start_kernel(const int32_t* __restrict__ cu, int n_seqs, int
 }
 
 // y = o / sqrt(mean(o^2) + eps) * SiLU(z), per (token, value head), fp16 out;
-// z is read from the projection rows (columns z_off + head * d)
+// z is read from the projection rows (columns z_off + head * D).  A wave
+// handles 4 rows, a lane D/64 adjacent elements of each; all loads of the 4
+// rows are issued before any arithmetic.
+template <int D>
 __global__ __launch_bounds__(256) void gated_norm_kernel(const _Float16* __restrict__ o,
                                                          const _Float16* __restrict__ P, int ldp,
-                                                         int z_off, int h_v, int rows, int d,
-                                                         float eps, _Float16* __restrict__ y) {
-  const int row = blockIdx.x * 4 + threadIdx.x / kWave;  // (token, head) row
+                                                         int z_off, int h_v, int rows, float eps,
+                                                         _Float16* __restrict__ y) {
+  constexpr int CPL = D / kWave, RPW = 4;
+  typedef _Float16 h2 __attribute__((ext_vector_type(CPL)));
   const int lane = threadIdx.x % kWave;
-  if (row >= rows) return;
-  const size_t base = static_cast<size_t>(row) * d;
-  const _Float16* z = P + static_cast<size_t>(row / h_v) * ldp + z_off + (row % h_v) * d;
-  float ss = 0.0f;
-  for (int c = lane; c < d; c += kWave) {
-    const float v = static_cast<float>(o[base + c]);
-    ss = fmaf(v, v, ss);
+  const int row0 = (blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * RPW;
+  h2 ov[RPW], zv[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = min(row0 + r, rows - 1);
+    ov[r] = *reinterpret_cast<const h2*>(o + static_cast<size_t>(row) * D + CPL * lane);
+    zv[r] = *reinterpret_cast<const h2*>(P + static_cast<size_t>(row / h_v) * ldp + z_off +
+                                         (row % h_v) * D + CPL * lane);
   }
 #pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-  const float inv = rsqrtf(ss / static_cast<float>(d) + eps);
-  for (int c = lane; c < d; c += kWave) {
-    const float zv = static_cast<float>(z[c]);
-    y[base + c] = static_cast<_Float16>(static_cast<float>(o[base + c]) * inv * silu(zv));
+  for (int r = 0; r < RPW; ++r) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) ss = fmaf(static_cast<float>(ov[r][e]), static_cast<float>(ov[r][e]), ss);
+    const float inv = rsqrtf(wave_sum(ss) / static_cast<float>(D) + eps);
+    h2 out;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e)
+      out[e] = static_cast<_Float16>(static_cast<float>(ov[r][e]) * inv * silu(static_cast<float>(zv[r][e])));
+    if (row0 + r < rows) *reinterpret_cast<h2*>(y + static_cast<size_t>(row0 + r) * D + CPL * lane) = out;
   }
 }
 
@@ -512,7 +532,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(const _Float16* __restr
 // workspace layout of one group call
 // ---------------------------------------------------------------------------
 struct Workspace {
-  size_t xres, xh, p, q, k, v, la, be, o, y, ss, total;
+  size_t xres, dres, xh, p, q, k, v, la, be, o, y, ss, total;
 };
 
 Workspace plan(const LayerShape& L, int T) {
@@ -525,6 +545,7 @@ Workspace plan(const LayerShape& L, int T) {
   };
   const size_t t = static_cast<size_t>(T);
   w.xres = take(t * L.hidden * 4);
+  w.dres = take(t * L.hidden * 4);
   w.xh = take(t * L.hidden * 2);
   w.p = take(t * L.n_all() * 2);
   w.q = take(t * L.h_k * L.d * 2);
@@ -539,9 +560,9 @@ Workspace plan(const LayerShape& L, int T) {
   return w;
 }
 
-template <int EPI, typename TX>
+template <int EPI>
 hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, int N, int K,
-                void* C, int ldc, const void* X, int ldx, hipStream_t s) {
+                void* C, int ldc, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   // the kernel addresses A and Bt with 32-bit byte offsets: split M so that
   // every launch stays below 2^31 bytes of A
@@ -554,12 +575,8 @@ hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, 
     void* Cm = EPI == EPI_STORE16
                    ? static_cast<void*>(static_cast<_Float16*>(C) + static_cast<size_t>(m_at) * ldc)
                    : static_cast<void*>(static_cast<float*>(C) + static_cast<size_t>(m_at) * ldc);
-    const void* Xm = X == nullptr ? nullptr
-                     : std::is_same<TX, F32>::value
-                         ? static_cast<const void*>(static_cast<const float*>(X) + static_cast<size_t>(m_at) * ldx)
-                         : static_cast<const void*>(static_cast<const uint16_t*>(X) + static_cast<size_t>(m_at) * ldx);
-    hipLaunchKernelGGL((gemm_kernel<EPI, TX>), grid, block, 0, s, A + static_cast<size_t>(m_at) * lda,
-                       lda, Bt, ldb, mm, N, K, Cm, ldc, Xm, ldx);
+    hipLaunchKernelGGL((gemm_kernel<EPI>), grid, block, 0, s, A + static_cast<size_t>(m_at) * lda,
+                       lda, Bt, ldb, mm, N, K, Cm, ldc);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -648,6 +665,7 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   float* xres = reinterpret_cast<float*>(ws + W.xres);
+  float* dres = reinterpret_cast<float*>(ws + W.dres);
   _Float16* xh = reinterpret_cast<_Float16*>(ws + W.xh);
   _Float16* P = reinterpret_cast<_Float16*>(ws + W.p);
   _Float16* qb = reinterpret_cast<_Float16*>(ws + W.q);
@@ -674,23 +692,28 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
     const _Float16* wout = reinterpret_cast<const _Float16*>(pk + L.win_bytes() + L.conv_bytes());
     float* st = states + state_stride * li;
     if (T > 0) {
-      // x of this layer: the anchors (bf16) for the first, the residual after;
+      // x of this layer: the anchors (bf16) for the first; after that the
+      // previous x plus the previous layer's output projection (dres), which
+      // this kernel adds and stores into the fp32 residual stream (xres);
       // xh = RMSNorm(x) in fp16, the A operand of the projection
-      const bool from_anchors = li == 0;
-      if (from_anchors)
-        hipLaunchKernelGGL(sr::rms_norm_kernel<sr::BF16>, dim3((T + 3) / 4), dim3(256), 0, s,
-                           anchors, T, d->hidden, d->rms_eps, xh);
+      const dim3 rgrid((T + 3) / 4);
+      if (li == 0)
+        hipLaunchKernelGGL((sr::rms_norm_kernel<sr::BF16, false>), rgrid, dim3(256), 0, s, anchors,
+                           nullptr, T, d->hidden, d->rms_eps, nullptr, xh);
+      else if (li == 1)
+        hipLaunchKernelGGL((sr::rms_norm_kernel<sr::BF16, true>), rgrid, dim3(256), 0, s, anchors,
+                           dres, T, d->hidden, d->rms_eps, xres, xh);
       else
-        hipLaunchKernelGGL(sr::rms_norm_kernel<sr::F32>, dim3((T + 3) / 4), dim3(256), 0, s,
-                           static_cast<const void*>(xres), T, d->hidden, d->rms_eps, xh);
+        hipLaunchKernelGGL((sr::rms_norm_kernel<sr::F32, true>), rgrid, dim3(256), 0, s,
+                           static_cast<const void*>(xres), dres, T, d->hidden, d->rms_eps, xres, xh);
       if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
       // the last layer needs k|v|a|b for its state, and q as well when its
       // conv window is returned (q follows the state prefix in the packing)
       const int N = !is_last ? L.n_all()
                   : conv_states ? static_cast<int>(sr::align_up(L.q_off() + d->h_k * d->d, 128))
                                 : L.n_state_pad();
-      if (sr::gemm<sr::EPI_STORE16, sr::F32>(xh, d->hidden, win, d->hidden, T, N, d->hidden, P,
-                                             L.n_all(), nullptr, 0, s) != hipSuccess)
+      if (sr::gemm<sr::EPI_STORE16>(xh, d->hidden, win, d->hidden, T, N, d->hidden, P, L.n_all(),
+                                    s) != hipSuccess)
         return SR_ELAUNCH;
       // conv heads: k, v (and q unless this is the last layer), then gates
       const int n_conv = is_last ? d->h_k + d->h_v : 2 * d->h_k + d->h_v;
@@ -738,14 +761,17 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
     if (sr::launch_gdn_chunk(g, s) != hipSuccess) return SR_ELAUNCH;
     if (is_last || T == 0) continue;
     const int rows = T * d->h_v;
-    hipLaunchKernelGGL(sr::gated_norm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, ob, P,
-                       L.n_all(), L.z_off(), d->h_v, rows, d->d, d->rms_eps, yb);
+    const dim3 ngrid((rows + 15) / 16);
+    if (d->d == 128)
+      hipLaunchKernelGGL(sr::gated_norm_kernel<128>, ngrid, dim3(256), 0, s, ob, P, L.n_all(),
+                         L.z_off(), d->h_v, rows, d->rms_eps, yb);
+    else
+      hipLaunchKernelGGL(sr::gated_norm_kernel<64>, ngrid, dim3(256), 0, s, ob, P, L.n_all(),
+                         L.z_off(), d->h_v, rows, d->rms_eps, yb);
     if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
     const int K2 = d->h_v * d->d;
-    hipError_t e = li == 0 ? sr::gemm<sr::EPI_RESID, sr::BF16>(yb, K2, wout, K2, T, d->hidden, K2,
-                                                               xres, d->hidden, anchors, d->hidden, s)
-                           : sr::gemm<sr::EPI_RESID, sr::F32>(yb, K2, wout, K2, T, d->hidden, K2,
-                                                              xres, d->hidden, xres, d->hidden, s);
+    // the residual add happens in the next layer's RMSNorm
+    hipError_t e = sr::gemm<sr::EPI_STORE32>(yb, K2, wout, K2, T, d->hidden, K2, dres, d->hidden, s);
     if (e != hipSuccess) return SR_ELAUNCH;
   }
   return SR_OK;

@@ -168,6 +168,26 @@ __device__ __forceinline__ f16x8 to_f16x8(f32x4 lo, f32x4 hi) {
   return cat44(to_f16x4(lo), to_f16x4(hi));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+  x += dpp_f32<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_f32<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_f32<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_f32<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_f32<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_f32<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+// Sum over the 64 lanes of a wave, returned to every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_inclusive_sum(x)), kWave - 1));
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
 __device__ __forceinline__ float softplus(float x) {
