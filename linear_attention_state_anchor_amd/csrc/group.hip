@@ -197,7 +197,8 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, const floa
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, so each XCD is
 // given a contiguous range of a grouped order (8 M-tiles wide, walking N):
 // the ~32 tiles an XCD runs at a time share 8 A and 4 B panels in its L2.
-// Requirements: K % 64 == 0, lda/ldb multiples of 8; M and N are guarded.
+// Requirements: K % 64 == 0, N % 4 == 0, lda/ldb/ldc multiples of 8; M and
+// N are guarded.
 // ---------------------------------------------------------------------------
 constexpr int EPI_STORE16 = 0;
 constexpr int EPI_STORE32 = 1;
@@ -273,11 +274,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
     for (int j = 0; j < 4; ++j)
       fb[j] = *reinterpret_cast<const f16x8*>(&sm[buf][1][(wn * 128 + 32 * j + l % 32) * GLD + 16 * ks + 8 * (l / 32)]);
   };
+  // C^T tiles (B fragment as the first operand): a lane then holds 4
+  // consecutive columns of one row, so the epilogue stores 4 values at once
   auto mma = [&](int h) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(av[h][i], bv[h][j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bv[h][j], av[h][i], acc[i][j]);
   };
 
   const int nk = K / GBK;
@@ -343,24 +346,26 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
-  // epilogue: lane holds column l%32 and rows 8(r/4) + 4(l/32) + r%4
+  // epilogue: lane holds row m = l%32 of fragment i and, in register group
+  // g = r/4, columns 8g + 4(l/32) .. +3 of fragment j
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + 32 * i + l % 32;
+    if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 128 + 32 * j + l % 32;
-      if (n >= N) continue;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 128 + 32 * i + 8 * (r / 4) + 4 * (l / 32) + (r % 4);
-        if (m >= M) continue;
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 128 + 32 * j + 8 * g + 4 * (l / 32);
+        if (n >= N) continue;  // N % 4 == 0: a group of 4 is in or out as a whole
         const size_t ci = static_cast<size_t>(m) * ldc + n;
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         if (EPI == EPI_STORE16)
-          static_cast<_Float16*>(C)[ci] = static_cast<_Float16>(acc[i][j][r]);
+          *reinterpret_cast<f16x4*>(static_cast<_Float16*>(C) + ci) = to_f16x4(v);
         else
-          static_cast<float*>(C)[ci] = acc[i][j][r];
+          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + ci) = v;
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
