@@ -377,10 +377,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
 // D/64 adjacent channels, so every row access is one coalesced 256-byte (or
 // 128-byte) wave load.  z is not copied: the gated RMSNorm reads it from P.
 // ---------------------------------------------------------------------------
-constexpr int FT = 64;   // tokens per workgroup
-constexpr int MAXW = 8;  // largest supported conv width
+constexpr int FT = 64;  // tokens per workgroup
 
-template <int D>
+// MAXW: conv widths up to MAXW (4 or 8); SiLU uses the hardware reciprocal
+template <int D, int MAXW>
 __global__ __launch_bounds__(256) void frontend_kernel(
     const _Float16* __restrict__ P, int ldp, LayerShape L, const float* __restrict__ convw,
     const int32_t* __restrict__ seq_start, int T, float l2_eps, int n_conv_heads,
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256) void frontend_kernel(
 #pragma unroll
       for (int k = 0; k < MAXW; ++k)  // row t-k is u[MAXW-1+i-k]
         if (k <= back) acc = fmaf(wt[e][k], static_cast<float>(u[MAXW - 1 + i - k][e]), acc);
-      y[e] = acc / (1.0f + __expf(-acc));  // SiLU
+      y[e] = acc * __builtin_amdgcn_rcpf(1.0f + __expf(-acc));  // SiLU
       ss = fmaf(y[e], y[e], ss);
     }
     if (kind != 1) {
@@ -723,12 +723,10 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
       // conv heads: k, v (and q unless this is the last layer), then gates
       const int n_conv = is_last ? d->h_k + d->h_v : 2 * d->h_k + d->h_v;
       const dim3 fgrid((T + sr::FT - 1) / sr::FT, n_conv + 1);
-      if (d->d == 128)
-        hipLaunchKernelGGL(sr::frontend_kernel<128>, fgrid, dim3(256), 0, s, P, L.n_all(), L, convw,
-                           sst, T, d->l2_eps, n_conv, qb, kb, vb, la, be);
-      else
-        hipLaunchKernelGGL(sr::frontend_kernel<64>, fgrid, dim3(256), 0, s, P, L.n_all(), L, convw,
-                           sst, T, d->l2_eps, n_conv, qb, kb, vb, la, be);
+      auto fe = d->d == 128 ? (L.width <= 4 ? sr::frontend_kernel<128, 4> : sr::frontend_kernel<128, 8>)
+                            : (L.width <= 4 ? sr::frontend_kernel<64, 4> : sr::frontend_kernel<64, 8>);
+      hipLaunchKernelGGL(fe, fgrid, dim3(256), 0, s, P, L.n_all(), L, convw, sst, T, d->l2_eps,
+                         n_conv, qb, kb, vb, la, be);
       if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
       if (conv_states) {
         hipLaunchKernelGGL(sr::conv_state_kernel, dim3(64, d->n_seqs), dim3(256), 0, s, P, L.n_all(),

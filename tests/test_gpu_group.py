@@ -67,6 +67,13 @@ def test_small_group(kinds):
     check(g)
 
 
+@pytest.mark.parametrize("width", [2, 6, 8])
+def test_conv_widths(width):
+    """Conv widths other than 4 (the wider ones take the 8-tap front end)."""
+    g = _group([70, 5, 129], 14 + width, 256, 2, 4, 128, [GDN, GDN], conv_width=width)
+    check(g)
+
+
 def test_group_hidden_2560_short():
     g = _group([130, 65, 1], 12, 2560, 16, 32, 128, [GDN, GDN, GDN, FA])
     check(g)
