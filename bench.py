@@ -262,8 +262,8 @@ def error_vs_k(to_dev, n_req=8, ks=(16, 32, 64, 128, 256, 512)):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-group", action="store_true")
@@ -361,7 +361,7 @@ def main():
         },
     }
     if not args.no_group:
-        line.update(bench_group(max(3, args.steps // 5), 2, to_dev))
+        line.update(bench_group(min(20, max(3, args.steps // 5)), 3, to_dev))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     if args.copy_calib:
