@@ -61,7 +61,7 @@ def _compile(src, force):
     if bad:
         os.remove(obj)
         raise RuntimeError(f"{src}: LDS transpose reads whose destination overlaps the "
-                           f"address register (wrong results on gfx950):\n" + "\n".join(bad))
+                           f"address register (kept out of the kernels):\n" + "\n".join(bad))
     return obj
 
 
@@ -71,11 +71,10 @@ _TR = re.compile(r"ds_read_b64_tr_b(?:16|8|4)\s+v\[(\d+):(\d+)\],\s*v(\d+)")
 def check_transpose_reads(asm: str) -> list:
     """Lines of `asm` where a ds_read_b64_tr_* writes its own address VGPR.
 
-    The hardware fetches the addresses of some lanes after writing part of
-    the result, so such an instruction reads from corrupted addresses.  The
-    compiler does not model this; the kernels keep their transpose-read bases
-    live across the reads, and this check makes the build fail if one slips
-    through."""
+    A build with that form gave wrong results in one kernel variant (the
+    cause is not established: an isolated test of the form did not show it).
+    The kernels keep their transpose-read bases live across the reads so the
+    form does not arise, and this check makes the build fail if it does."""
     bad, func = [], "?"
     for line in asm.splitlines():
         if line and not line[0].isspace() and line.endswith(":") and not line.startswith("."):

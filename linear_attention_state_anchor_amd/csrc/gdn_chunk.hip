@@ -89,15 +89,17 @@ __device__ __forceinline__ f16x4 lds4(const _Float16* p) {
 // therefore passes  base + (l/4)*S + 4*(l%4)  to read rows R0+4(l/16)..+3 at
 // column C0 + l%16, where base points at (R0, C0).
 //
-// The destination of a transpose read must not overlap its address register:
-// the hardware reads the addresses of the lanes supplying rows 2-3 after it
-// has written rows 0-1, so an overlapping destination corrupts the read.  The
-// compiler does not know this, so every transpose read goes through a base
-// address that (i) comes out of an opaque copy (tr_base), which the register
-// allocator cannot rematerialise into a fresh register, and (ii) stays live
-// until after the last read that uses it (tr_keep).  The offset argument is a
-// compile-time constant after unrolling and folds into the instruction.  The
-// build scans the generated code and fails if any overlap remains.
+// Transpose reads here never write their own address register.  A build in
+// which the register allocator chose that form (destination overlapping the
+// address) returned wrong rows in the d = 64 state-only kernel; a one-wave
+// test of the same instruction form did not reproduce it, so the cause is not
+// established, and the form is kept out as a precaution: every transpose
+// read goes through a base address that (i) comes out of an opaque copy
+// (tr_base), which the register allocator cannot rematerialise into a fresh
+// register, and (ii) stays live until after the last read that uses it
+// (tr_keep).  The offset argument is a compile-time constant after unrolling
+// and folds into the instruction.  The build scans the generated code and
+// fails if the form appears.
 __device__ __forceinline__ uint32_t tr_base(uint32_t lds_byte_addr) {
   uint32_t b;
   asm volatile("" : "=v"(b) : "0"(lds_byte_addr));
