@@ -54,34 +54,67 @@ def _compile(src, force):
              if f.startswith((stem + "-hip-", stem + "-host-", stem + ".hip-hip-"))]
     try:
         asm = os.path.join(BUILD, f"{stem}-hip-amdgcn-amd-amdhsa-{ARCH}.s")
-        bad = check_transpose_reads(open(asm).read())
+        bad = check_mfma_chains(open(asm).read())
     finally:
         for t in temps:
             os.remove(t)
     if bad:
         os.remove(obj)
-        raise RuntimeError(f"{src}: LDS transpose reads whose destination overlaps the "
-                           f"address register (kept out of the kernels):\n" + "\n".join(bad))
+        raise RuntimeError(f"{src}: MFMA accumulation chains that mix shapes without enough "
+                           f"wait states (stale accumulators on gfx950):\n" + "\n".join(bad))
     return obj
 
 
-_TR = re.compile(r"ds_read_b64_tr_b(?:16|8|4)\s+v\[(\d+):(\d+)\],\s*v(\d+)")
+_MFMA = re.compile(r"(v_mfma_\w+)\s+([va]\[\d+:\d+\]|[va]\d+),\s*([va]\[\d+:\d+\]|[va]\d+),\s*"
+                   r"([va]\[\d+:\d+\]|[va]\d+),\s*([va]\[\d+:\d+\]|[va]\d+|[-\w.]+)")
+_REGS = re.compile(r"([va])\[(\d+):(\d+)\]|([va])(\d+)\b")
+_NOP = re.compile(r"s_nop\s+(\d+)")
+MFMA_CHAIN_WAIT_STATES = 8
 
 
-def check_transpose_reads(asm: str) -> list:
-    """Lines of `asm` where a ds_read_b64_tr_* writes its own address VGPR.
+def _regs(tok: str) -> set:
+    out = set()
+    for m in _REGS.finditer(tok):
+        if m.group(1):
+            out |= {(m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+        else:
+            out.add((m.group(4), int(m.group(5))))
+    return out
 
-    A build with that form gave wrong results in one kernel variant (the
-    cause is not established: an isolated test of the form did not show it).
-    The kernels keep their transpose-read bases live across the reads so the
-    form does not arise, and this check makes the build fail if it does."""
+
+def check_mfma_chains(asm: str, min_wait_states: int = MFMA_CHAIN_WAIT_STATES) -> list:
+    """Lines of `asm` where an MFMA accumulates (SrcC) onto the result of an
+    earlier MFMA of a different shape with fewer than `min_wait_states` wait
+    states between them.
+
+    On gfx950 such a pair (e.g. 16x16x32 f16 then 16x16x16 f16 on the same
+    accumulator) reads two stale accumulator registers unless about five
+    wait states separate the two; the compiler inserts one.  Chains of one
+    shape are safe.  The kernels avoid mixed chains; this scan makes the build
+    fail if one appears.  Wait states: one per instruction, N + 1 per s_nop N;
+    a VALU/memory write to the accumulator in between ends the chain."""
     bad, func = [], "?"
+    last = []  # (opcode, dst regs, wait states since), most recent last
     for line in asm.splitlines():
         if line and not line[0].isspace() and line.endswith(":") and not line.startswith("."):
-            func = line[:-1]
-        m = _TR.search(line)
-        if m and int(m.group(1)) <= int(m.group(3)) <= int(m.group(2)):
-            bad.append(f"{func}: {line.strip()}")
+            func, last = line[:-1], []
+            continue
+        ins = line.strip()
+        if not ins or ins.startswith((";", ".")) or ins.endswith(":"):
+            continue
+        m = _MFMA.match(ins)
+        n = _NOP.match(ins)
+        step = int(n.group(1)) + 1 if n else 1
+        if m:
+            op, dst, src_c = m.group(1), _regs(m.group(2)), _regs(m.group(5))
+            for pop, pdst, ws in last:
+                if pop != op and pdst & src_c and ws < min_wait_states:
+                    bad.append(f"{func}: {ins}  (accumulates onto {pop} {ws} wait states earlier)")
+            last = [(o, d - dst, w) for o, d, w in last if d - dst]
+            last = [(o, d, w + 1) for o, d, w in last] + [(op, dst, 0)]
+        else:
+            written = _regs(ins.split(",")[0].split(None, 1)[1]) if ("," in ins and ins.startswith(("v_", "ds_read", "global_load", "buffer_load", "scratch_load", "flat_load"))) else set()
+            last = [(o, d - written, w + step) for o, d, w in last if d - written]
     return bad
 
 

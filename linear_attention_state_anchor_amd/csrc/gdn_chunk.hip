@@ -17,9 +17,9 @@
 // each), then block row i of [W | U~] is (I + A_ii)^{-1} (R_i - sum_{m<i}
 // A_im Y_m), all on the matrix cores with register-resident operands.
 //
-// Work layout: one workgroup (4 waves) per (sequence, value head) walks the
+// Work layout: one workgroup of NW waves per (sequence, value head) walks the
 // sequence's chunks in order; wave w owns value columns and key columns
-// [w*D/4, (w+1)*D/4).  The transposed state S^T (d_k x d_v, fp32) stays in
+// [w*D/NW, (w+1)*D/NW).  The transposed state S^T (d_k x d_v, fp32) stays in
 // accumulator registers for the whole sequence.  Accumulator tiles feed later
 // products directly as operands: two vertically adjacent 16x16 tiles hold,
 // per lane, the k-slots {4g..4g+3, 16+4g..16+4g+3} (g = lane/16) of a K = 32
@@ -37,7 +37,11 @@ namespace sr {
 namespace {
 
 constexpr int kC = 64;         // chunk length (tokens)
-constexpr int kThreads = 256;  // 4 waves
+// Waves per workgroup (the code also supports 8 at d = 128: 16 value
+// columns per wave; measured slower there, as the register budget of four
+// waves per SIMD forces spills).  Two workgroups share a CU (LDS-bound).
+template <int D>
+constexpr int kWaves = 4;
 constexpr int kAS = kC + 8;    // fp16 row stride of -A
 constexpr int kPS = kC + 4;    // fp16 row stride of P o QK^T
 constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
@@ -89,17 +93,11 @@ __device__ __forceinline__ f16x4 lds4(const _Float16* p) {
 // therefore passes  base + (l/4)*S + 4*(l%4)  to read rows R0+4(l/16)..+3 at
 // column C0 + l%16, where base points at (R0, C0).
 //
-// Transpose reads here never write their own address register.  A build in
-// which the register allocator chose that form (destination overlapping the
-// address) returned wrong rows in the d = 64 state-only kernel; a one-wave
-// test of the same instruction form did not reproduce it, so the cause is not
-// established, and the form is kept out as a precaution: every transpose
-// read goes through a base address that (i) comes out of an opaque copy
-// (tr_base), which the register allocator cannot rematerialise into a fresh
-// register, and (ii) stays live until after the last read that uses it
-// (tr_keep).  The offset argument is a compile-time constant after unrolling
-// and folds into the instruction.  The build scans the generated code and
-// fails if the form appears.
+// Every transpose read of a tile goes through one base address that comes
+// out of an opaque copy (tr_base), so the compiler keeps it in a single
+// register instead of rematerialising it per read, and stays live until after
+// the last read (tr_keep); the offset argument is a compile-time constant
+// after unrolling and folds into the instruction.
 __device__ __forceinline__ uint32_t tr_base(uint32_t lds_byte_addr) {
   uint32_t b;
   asm volatile("" : "=v"(b) : "0"(lds_byte_addr));
@@ -159,28 +157,36 @@ __device__ __forceinline__ float raw_to_f32<F16>(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
-// Tile jobs of wave W for one chunk: the diagonal block A_WW (erase mode)
-// followed by the inverse (I + A_WW)^{-1}, then every fourth of the
-// off-diagonal A tiles and the lower P o QK^T tiles.  The job list is fixed at
-// compile time so the whole section is straight-line code with immediate
-// LDS offsets, and the k-steps of all jobs interleave.
+// Tile jobs of wave W for one chunk.  Waves 0..3 each form a diagonal block
+// A_WW (erase mode) and invert I + A_WW.  With 4 waves, wave W also takes
+// jobs W, W+4, W+8, W+12 of the list below; with 8 waves, waves 0..3 take
+// one job each (12..15) and waves 4..7 the other twelve, three each.  The job
+// list is fixed at compile time so the whole section is straight-line code
+// with immediate LDS offsets, and the k-steps of all jobs interleave.
 //   A tile jobs:        (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 //   P o QK^T tile jobs: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-template <int D, bool ERASE, bool WANT_O, int W>
+template <int D, bool ERASE, bool WANT_O, int W, int NW>
 __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
   constexpr int NKJ = D / 32;
   constexpr int kJob[16][3] = {{1, 1, 0}, {1, 2, 0}, {1, 2, 1}, {1, 3, 0}, {1, 3, 1}, {1, 3, 2},
                                {0, 0, 0}, {0, 1, 0}, {0, 1, 1}, {0, 2, 0}, {0, 2, 1}, {0, 2, 2},
                                {0, 3, 0}, {0, 3, 1}, {0, 3, 2}, {0, 3, 3}};
-  // slot 0: the diagonal A block; slots 1..4: jobs W, W+4, W+8, W+12
-  auto slot_on = [](int q) constexpr {
-    if (q == 0) return ERASE;
-    const int j = W + 4 * (q - 1);
+  constexpr bool kDiag = ERASE && W < 4;
+  // slot 0: the diagonal A block; slots 1..4: this wave's jobs (-1: none)
+  auto job = [](int q) constexpr {
+    if (NW == 4) return W + 4 * (q - 1);
+    if (W < 4) return q == 1 ? 12 + W : -1;
+    return q <= 3 ? (W - 4) + 4 * (q - 1) : -1;
+  };
+  auto slot_on = [job](int q) constexpr {
+    if (q == 0) return kDiag;
+    const int j = job(q);
+    if (j < 0) return false;
     return kJob[j][0] == 1 ? ERASE : WANT_O;
   };
-  auto slot_kk = [](int q) constexpr { return q == 0 || kJob[W + 4 * (q - 1)][0] == 1; };
-  auto slot_tr = [](int q) constexpr { return q == 0 ? W : kJob[W + 4 * (q - 1)][1]; };
-  auto slot_tc = [](int q) constexpr { return q == 0 ? W : kJob[W + 4 * (q - 1)][2]; };
+  auto slot_kk = [job](int q) constexpr { return q == 0 || kJob[job(q)][0] == 1; };
+  auto slot_tr = [job](int q) constexpr { return q == 0 ? W : kJob[job(q)][1]; };
+  auto slot_tc = [job](int q) constexpr { return q == 0 ? W : kJob[job(q)][2]; };
   f32x4 acc[5];
 #pragma unroll
   for (int q = 0; q < 5; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -213,7 +219,7 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
         sm.pqk[row * kPS + col] = static_cast<_Float16>(row >= col ? dgam * acc[q][r] : 0.0f);
     }
   }
-  if (ERASE) {
+  if (kDiag) {
     // (I + A_WW)^{-1} by forward substitution in fp32, lane column lr; the
     // block's rows come back from LDS as broadcast reads (this wave wrote
     // them, so no barrier is needed)
@@ -235,15 +241,19 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
 }
 
 template <int D, typename TI, typename TO, bool ERASE, bool WANT_O>
-__global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
-  constexpr int IW = D / 4;       // value (and key) columns per wave
+__global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kernel(GdnArgs a,
+                                                                                  int units_per_xcd) {
+  constexpr int NW = kWaves<D>;
+  constexpr int kThreads = 64 * NW;
+  constexpr int IW = D / NW;      // value (and key) columns per wave
   constexpr int NIT = IW / 16;    // 16-wide column tiles per wave
   constexpr int NJT = D / 16;     // 16-wide key tiles
   constexpr int NKJ = D / 32;     // K = 32 steps over the key dimension
   constexpr int CPR = D / 8;      // 16-byte chunks per row
-  constexpr int NPF = CPR / 4;    // 16-byte K (and Q) row pieces per thread
+  constexpr int NPF = kC * CPR / kThreads;  // 16-byte K (and Q) row pieces per thread
   constexpr int kWS = ChunkSmem<D>::kWS;
-  static_assert(NIT >= 1, "D too small");
+  static_assert(NIT >= 1 && IW % 16 == 0, "D too small");
+  static_assert(kC * CPR % kThreads == 0, "staging pieces must divide evenly");
 
   __shared__ ChunkSmem<D> sm;
 
@@ -406,14 +416,18 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
     }
 
     // ---- A (erase) and P o QK^T: lower-triangular 16x16 tiles -------------
-    // Wave w first forms the diagonal block A_ww and inverts I + A_ww itself
-    // (wave-local LDS round trip, no barrier), then takes its share of the
-    // off-diagonal A tiles and the P o QK^T tiles.
+    // Waves 0..3 form the diagonal blocks A_ww and invert I + A_ww (a
+    // wave-local LDS round trip, no barrier); every wave takes its share of
+    // the off-diagonal A tiles and the P o QK^T tiles.
     switch (w) {
-      case 0: chunk_tiles<D, ERASE, WANT_O, 0>(sm, lr, lg); break;
-      case 1: chunk_tiles<D, ERASE, WANT_O, 1>(sm, lr, lg); break;
-      case 2: chunk_tiles<D, ERASE, WANT_O, 2>(sm, lr, lg); break;
-      default: chunk_tiles<D, ERASE, WANT_O, 3>(sm, lr, lg); break;
+      case 0: chunk_tiles<D, ERASE, WANT_O, 0, NW>(sm, lr, lg); break;
+      case 1: chunk_tiles<D, ERASE, WANT_O, 1, NW>(sm, lr, lg); break;
+      case 2: chunk_tiles<D, ERASE, WANT_O, 2, NW>(sm, lr, lg); break;
+      case 3: chunk_tiles<D, ERASE, WANT_O, 3, NW>(sm, lr, lg); break;
+      case 4: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 4, NW>(sm, lr, lg); break;
+      case 5: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 5, NW>(sm, lr, lg); break;
+      case 6: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 6, NW>(sm, lr, lg); break;
+      default: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 7, NW>(sm, lr, lg); break;
     }
     __syncthreads();
 
@@ -462,9 +476,15 @@ __global__ __launch_bounds__(kThreads, 2) void gdn_chunk_kernel(GdnArgs a, int u
           for (int ct = 0; ct < 2 * NIT; ++ct)
             X[ct] = mfma16x16x32(a8, cat44(yprev(0, ct), yprev(1, ct)), X[ct]);
           if (bi == 3) {
-            const f16x4 a4 = lds4(arow + 32 + 4 * lg);
+            // the third term as a K = 32 product with zero upper k-slots:
+            // accumulating a 16x16x16 MFMA onto a 16x16x32 result (or the
+            // reverse) reads two stale accumulator registers on gfx950 unless
+            // about five wait states separate them, which the compiler does
+            // not insert; same-shape accumulation chains are safe
+            const f16x4 z4 = {};
+            const f16x8 a8z = cat44(lds4(arow + 32 + 4 * lg), z4);
 #pragma unroll
-            for (int ct = 0; ct < 2 * NIT; ++ct) X[ct] = mfma16x16x16(a4, yprev(2, ct), X[ct]);
+            for (int ct = 0; ct < 2 * NIT; ++ct) X[ct] = mfma16x16x32(a8z, cat44(yprev(2, ct), z4), X[ct]);
           }
         }
         const f16x4 t4 = lds4(&sm.td[bi * 256 + lr * 16 + 4 * lg]);
@@ -629,7 +649,7 @@ template <int D, typename TI, typename TO>
 hipError_t launch3(const GdnArgs& a, hipStream_t s) {
   const int units = a.n_seqs * a.h_v;
   const int per_xcd = (units + kXcd - 1) / kXcd;
-  dim3 grid(per_xcd * kXcd), block(kThreads);
+  dim3 grid(per_xcd * kXcd), block(64 * kWaves<D>);
   const bool o = a.o != nullptr;
   if (a.erase && o)
     hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true>), grid, block, 0, s, a, per_xcd);
