@@ -142,6 +142,64 @@ def timed(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def time_launches(fn, steps, warmup):
+    """Average milliseconds per call of fn over `steps` calls, HIP events on
+    the current stream (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def replay_entry(ms, T, byts, flops):
+    sec = ms / 1e3
+    return {"ms_per_step": ms, "replayed_tokens_per_s": T / sec,
+            "hbm_gbs": byts / sec / 1e9, "hbm_frac": byts / sec / 1e9 / HBM_PEAK_GBS,
+            "mfma_tflops": flops / sec / 1e12,
+            "mfma_frac": flops / sec / 1e12 / MFMA_F16_PEAK_TFS,
+            "bytes_per_launch": byts, "flop_per_launch": flops}
+
+
+def bench_replay_variants(steps, warmup, to_dev, q, k, v, alpha, beta, cu, S):
+    """Secondary single-layer replay measurements: the headline workload in
+    state-only mode (no q, no o: the last layer of a group), and the
+    erase-free (scalar-decay) 8 x 2048, 32-head workload with outputs."""
+    import torch
+    import linear_attention_state_anchor_amd as sr
+    from replay_inputs import config_c2
+
+    n, L, hk, hv, d = S.shape[0], 3276, k.shape[1], v.shape[1], k.shape[2]
+    T = k.shape[0]
+    ms = time_launches(lambda: sr.gdn_replay_state(None, k, v, alpha, beta, cu, None,
+                                                   alpha_is_log=True, want_o=False,
+                                                   final_state=S), steps, warmup)
+    byts, flops = gdn_algorithmic(n, L, hk, hv, d, want_o=False)
+    out = {"state_only": dict(workload="headline replay without q and o (state only)",
+                              **replay_entry(ms, T, byts, flops))}
+    c = config_c2()
+    q2, k2, v2, a2, cu2 = (to_dev(x) for x in (c.q, c.k, c.v, c.alpha, c.cu_seqlens))
+    S2 = torch.empty((c.n_seqs, c.h_v, c.d_k, c.d_v), dtype=torch.float32, device=k.device)
+    o2 = torch.empty((c.total_tokens, c.h_v, c.d_v), dtype=torch.bfloat16, device=k.device)
+    ms = time_launches(lambda: sr.gdn_replay_state(q2, k2, v2, a2, None, cu2, None, erase=False,
+                                                   alpha_is_log=c.alpha_is_log,
+                                                   final_state=S2, o=o2), steps, warmup)
+    byts, flops = gdn_algorithmic(c.n_seqs, c.total_tokens // c.n_seqs, c.h_k, c.h_v, c.d_k,
+                                  erase=False)
+    out["erase_free"] = dict(workload="erase-free (scalar decay) replay, 8 x 2048, 32 heads, "
+                                      "d=128, bf16 in/out, beta = 1",
+                             **replay_entry(ms, c.total_tokens, byts, flops))
+    return out
+
+
 def bench_group(steps, warmup, to_dev):
     """3-layer replay group (hidden 2560) from 4 x 1638 anchors, and the
     varlen path: 64 hits gathered from a paged pool of full prefixes and
@@ -360,6 +418,8 @@ def main():
             "bytes_per_launch": byts,
         },
     }
+    line.update(bench_replay_variants(min(50, args.steps), 10, to_dev, q, k, v, alpha, beta,
+                                      cu, S))
     if not args.no_group:
         line.update(bench_group(min(20, max(3, args.steps // 5)), 3, to_dev))
     if not args.no_cpu_baseline:
