@@ -55,18 +55,22 @@ struct ChunkSmem {
   static constexpr int kKS = D + 16;  // K rows
   static constexpr int kQS = D + 8;   // Q rows
   static constexpr int kWS = D + 8;   // V / -W rows
-  _Float16 k[kC * kKS];              // K rows
-  _Float16 q[kC * kQS];              // Q rows
-  _Float16 a[kC * kAS];              // -A (strictly lower off-diagonal blocks)
-  uint16_t w[kC * kWS];              // raw V rows at staging, overwritten by -W (fp16)
-  _Float16 pqk[kC * kPS];            // P o (Q K^T)
-  _Float16 td[4 * 16 * 16];          // (I + A_bb)^{-1}, row-major per block
-  float dg[4 * 16 * 16];             // A_bb, fp32, row-major per block
+  // Order: everything read with compile-time offsets lies below 64 KB, so a
+  // DS instruction's 16-bit offset field holds the array start and one base
+  // register serves many reads; K (last) is read through opaque per-lane
+  // bases.  Every array starts on a 256-byte boundary (bank-neutral).
   float gcum[kC];                    // G_t
   float gam[kC];                     // e^{G_t}
   float dec[kC];                     // e^{G_C - G_t}
   float beta[kC];                    // b_t (0 past the end of the sequence)
   float bg[kC];                      // b_t e^{G_t}
+  _Float16 td[4 * 16 * 16];          // (I + A_bb)^{-1}, row-major per block
+  float dg[4 * 16 * 16];             // A_bb, fp32, row-major per block
+  _Float16 a[kC * kAS];              // -A (strictly lower off-diagonal blocks)
+  _Float16 pqk[kC * kPS];            // P o (Q K^T)
+  _Float16 q[kC * kQS];              // Q rows
+  uint16_t w[kC * kWS];              // raw V rows at staging, overwritten by -W (fp16)
+  _Float16 k[kC * kKS];              // K rows
 };
 
 // element (t, j) of the padded K and Q row tiles
@@ -115,6 +119,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
 __device__ __forceinline__ f16x4 as_f16x4(u16x4 v) { return __builtin_bit_cast(f16x4, v); }
+// 16-byte LDS read at an opaque base plus a compile-time byte offset.
+__device__ __forceinline__ f16x8 lds8_at(uint32_t base, int byte_off) {
+  return *(const __attribute__((address_space(3))) f16x8*)(static_cast<uintptr_t>(base + byte_off));
+}
 
 __device__ __forceinline__ f32x4 mfma16x16x16(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
@@ -190,17 +198,22 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
   f32x4 acc[5];
 #pragma unroll
   for (int q = 0; q < 5; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this lane's row lr, k-slots 8lg.. of the K and Q tiles
+  const uint32_t kl = tr_base(lds_addr(&sm.k[kidx<D>(lr, 8 * lg)]));
+  const uint32_t ql = WANT_O ? tr_base(lds_addr(&sm.q[qidx<D>(lr, 8 * lg)])) : 0u;
 #pragma unroll
   for (int ks = 0; ks < NKJ; ++ks) {
 #pragma unroll
     for (int q = 0; q < 5; ++q) {
       if (!slot_on(q)) continue;
-      const f16x8 av = slot_kk(q) ? lds8(&sm.k[kidx<D>(16 * slot_tr(q) + lr, 32 * ks + 8 * lg)])
-                                  : lds8(&sm.q[qidx<D>(16 * slot_tr(q) + lr, 32 * ks + 8 * lg)]);
-      const f16x8 bv = lds8(&sm.k[kidx<D>(16 * slot_tc(q) + lr, 32 * ks + 8 * lg)]);
+      const f16x8 av = slot_kk(q) ? lds8_at(kl, 2 * kidx<D>(16 * slot_tr(q), 32 * ks))
+                                  : lds8_at(ql, 2 * qidx<D>(16 * slot_tr(q), 32 * ks));
+      const f16x8 bv = lds8_at(kl, 2 * kidx<D>(16 * slot_tc(q), 32 * ks));
       acc[q] = mfma16x16x32(av, bv, acc[q]);
     }
   }
+  tr_keep(kl);
+  if (WANT_O) tr_keep(ql);
   // epilogues: masked, decay-weighted tiles to LDS (the diagonal A block in
   // fp32 for the inverse)
 #pragma unroll
