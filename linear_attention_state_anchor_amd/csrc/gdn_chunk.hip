@@ -43,7 +43,7 @@ constexpr int kC = 64;         // chunk length (tokens)
 template <int D>
 constexpr int kWaves = 4;
 constexpr int kAS = kC + 8;    // fp16 row stride of -A
-constexpr int kPS = kC + 4;    // fp16 row stride of P o QK^T
+constexpr int kPS = kC + 8;    // fp16 row stride of P o QK^T
 constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
 
 template <int D>
@@ -72,6 +72,14 @@ struct ChunkSmem {
   uint16_t w[kC * kWS];              // raw V rows at staging, overwritten by -W (fp16)
   _Float16 k[kC * kKS];              // K rows
 };
+
+// Storage position of column c in tiles that are read only as K = 32 MFMA
+// operands (-A, P o QK^T and -W): a K = 32 operand gives lane group g the
+// k-slots {4g..4g+3, 16+4g..16+4g+3} of each 32-column group, which this
+// order stores next to each other, so one 16-byte read fetches them.
+__device__ __forceinline__ constexpr int kperm(int c) {
+  return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c & 31) >> 4) + (c & 3);
+}
 
 // element (t, j) of the padded K and Q row tiles
 template <int D>
@@ -227,9 +235,9 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
       if (q == 0)
         sm.dg[W * 256 + (4 * lg + r) * 16 + lr] = row > col ? sm.beta[row] * dgam * acc[q][r] : 0.0f;
       else if (slot_kk(q))
-        sm.a[row * kAS + col] = static_cast<_Float16>(row > col ? -(sm.beta[row] * dgam * acc[q][r]) : 0.0f);
+        sm.a[row * kAS + kperm(col)] = static_cast<_Float16>(row > col ? -(sm.beta[row] * dgam * acc[q][r]) : 0.0f);
       else
-        sm.pqk[row * kPS + col] = static_cast<_Float16>(row >= col ? dgam * acc[q][r] : 0.0f);
+        sm.pqk[row * kPS + kperm(col)] = static_cast<_Float16>(row >= col ? dgam * acc[q][r] : 0.0f);
     }
   }
   if (kDiag) {
@@ -267,6 +275,10 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
   constexpr int kWS = ChunkSmem<D>::kWS;
   static_assert(NIT >= 1 && IW % 16 == 0, "D too small");
   static_assert(kC * CPR % kThreads == 0, "staging pieces must divide evenly");
+  // -W is stored in K = 32 operand order only when each wave's columns form
+  // whole 32-column groups (the permutation must not move a wave's -W into
+  // another wave's V columns before that wave has read them)
+  constexpr bool kPermW = IW % 32 == 0;
 
   __shared__ ChunkSmem<D> sm;
 
@@ -306,8 +318,8 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
   // the output product and never written otherwise
   for (int e = tid; e < 256; e += kThreads) {
     const int rr = e / 16, cc = e % 16;
-    sm.pqk[rr * kPS + 16 + cc] = static_cast<_Float16>(0.0f);
-    sm.pqk[(32 + rr) * kPS + 48 + cc] = static_cast<_Float16>(0.0f);
+    sm.pqk[rr * kPS + kperm(16 + cc)] = static_cast<_Float16>(0.0f);
+    sm.pqk[(32 + rr) * kPS + kperm(48 + cc)] = static_cast<_Float16>(0.0f);
   }
 
   const int t_begin = a.cu[n];
@@ -480,11 +492,11 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
         }
         const _Float16* arow = &sm.a[(16 * bi + lr) * kAS];
         if (bi == 1) {
-          const f16x4 a4 = lds4(arow + 4 * lg);
+          const f16x4 a4 = lds4(arow + 8 * lg);
 #pragma unroll
           for (int ct = 0; ct < 2 * NIT; ++ct) X[ct] = mfma16x16x16(a4, yprev(0, ct), X[ct]);
         } else if (bi >= 2) {
-          const f16x8 a8 = cat44(lds4(arow + 4 * lg), lds4(arow + 16 + 4 * lg));
+          const f16x8 a8 = lds8(arow + 8 * lg);
 #pragma unroll
           for (int ct = 0; ct < 2 * NIT; ++ct)
             X[ct] = mfma16x16x32(a8, cat44(yprev(0, ct), yprev(1, ct)), X[ct]);
@@ -495,7 +507,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
             // about five wait states separate them, which the compiler does
             // not insert; same-shape accumulation chains are safe
             const f16x4 z4 = {};
-            const f16x8 a8z = cat44(lds4(arow + 32 + 4 * lg), z4);
+            const f16x8 a8z = cat44(lds4(arow + 32 + 8 * lg), z4);
 #pragma unroll
             for (int ct = 0; ct < 2 * NIT; ++ct) X[ct] = mfma16x16x32(a8z, cat44(yprev(2, ct), z4), X[ct]);
           }
@@ -510,7 +522,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
             if (bi < 3) Wh[bi][ct] = yh;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              sm.w[(16 * bi + 4 * lg + r) * kWS + j] = f16_bits(-yh[r]);
+              sm.w[(16 * bi + 4 * lg + r) * kWS + (kPermW ? kperm(j) : j)] = f16_bits(-yh[r]);
           } else {
             U[bi][ct - NIT] = y;
           }
@@ -546,7 +558,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const _Float16* wr = reinterpret_cast<const _Float16*>(&sm.w[(16 * tt + lr) * kWS + 32 * kk]);
-          const f16x8 av = cat44(lds4(wr + 4 * lg), lds4(wr + 16 + 4 * lg));
+          const f16x8 av = kPermW ? lds8(wr + 8 * lg) : cat44(lds4(wr + 4 * lg), lds4(wr + 16 + 4 * lg));
 #pragma unroll
           for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(av, s16[it], U[tt][it]);
         }
@@ -608,7 +620,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
           for (int ks = 0; ks < 2; ++ks) {
             if (32 * ks > 16 * tt + 15) continue;  // P o QK^T is lower triangular
             const _Float16* pr = &sm.pqk[t * kPS + 32 * ks];
-            const f16x8 pb = cat44(lds4(pr + 4 * lg), lds4(pr + 16 + 4 * lg));
+            const f16x8 pb = lds8(pr + 8 * lg);
 #pragma unroll
             for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(U16[ks][it], pb, O[u][it]);
           }
