@@ -67,7 +67,7 @@ struct ChunkSmem {
   _Float16 td[4 * 16 * 16];          // (I + A_bb)^{-1}, row-major per block
   float dg[4 * 16 * 16];             // A_bb, fp32, row-major per block
   _Float16 a[kC * kAS];              // -A (strictly lower off-diagonal blocks)
-  _Float16 pqk[kC * kPS];            // P o (Q K^T)
+  _Float16 pqk[kC * kPS];            // scale * P o (Q K^T)
   _Float16 q[kC * kQS];              // Q rows
   uint16_t w[kC * kWS];              // raw V rows at staging, overwritten by -W (fp16)
   _Float16 k[kC * kKS];              // K rows
@@ -182,7 +182,7 @@ __device__ __forceinline__ float raw_to_f32<F16>(uint16_t b) {
 //   A tile jobs:        (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 //   P o QK^T tile jobs: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
 template <int D, bool ERASE, bool WANT_O, int W, int NW>
-__device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
+__device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, float scale) {
   constexpr int NKJ = D / 32;
   constexpr int kJob[16][3] = {{1, 1, 0}, {1, 2, 0}, {1, 2, 1}, {1, 3, 0}, {1, 3, 1}, {1, 3, 2},
                                {0, 0, 0}, {0, 1, 0}, {0, 1, 1}, {0, 2, 0}, {0, 2, 1}, {0, 2, 2},
@@ -237,7 +237,7 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg) {
       else if (slot_kk(q))
         sm.a[row * kAS + kperm(col)] = static_cast<_Float16>(row > col ? -(sm.beta[row] * dgam * acc[q][r]) : 0.0f);
       else
-        sm.pqk[row * kPS + kperm(col)] = static_cast<_Float16>(row >= col ? dgam * acc[q][r] : 0.0f);
+        sm.pqk[row * kPS + kperm(col)] = static_cast<_Float16>(row >= col ? scale * dgam * acc[q][r] : 0.0f);
     }
   }
   if (kDiag) {
@@ -406,13 +406,13 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     // per address for the whole sequence).
     int tro, trv;  // this lane's transpose-read offsets in the K and V tiles
     {
-      int t_ = tid;
+      unsigned t_ = tid;
       asm volatile("" : "+v"(t_));
-      l = t_ % kWave;
-      lr = t_ % 16;
-      lg = (t_ / 16) % 4;
-      tro = (l / 4) * ChunkSmem<D>::kKS + 4 * (l % 4);
-      trv = (l / 4) * kWS + 4 * (l % 4);
+      l = t_ & (kWave - 1);
+      lr = t_ & 15;
+      lg = (t_ >> 4) & 3;
+      tro = (l >> 2) * ChunkSmem<D>::kKS + 4 * (l & 3);
+      trv = (l >> 2) * kWS + 4 * (l & 3);
     }
 
     // ---- stage this chunk: K, Q, V rows (already fp16) and gate scalars --
@@ -445,14 +445,14 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     // wave-local LDS round trip, no barrier); every wave takes its share of
     // the off-diagonal A tiles and the P o QK^T tiles.
     switch (w) {
-      case 0: chunk_tiles<D, ERASE, WANT_O, 0, NW>(sm, lr, lg); break;
-      case 1: chunk_tiles<D, ERASE, WANT_O, 1, NW>(sm, lr, lg); break;
-      case 2: chunk_tiles<D, ERASE, WANT_O, 2, NW>(sm, lr, lg); break;
-      case 3: chunk_tiles<D, ERASE, WANT_O, 3, NW>(sm, lr, lg); break;
-      case 4: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 4, NW>(sm, lr, lg); break;
-      case 5: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 5, NW>(sm, lr, lg); break;
-      case 6: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 6, NW>(sm, lr, lg); break;
-      default: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 7, NW>(sm, lr, lg); break;
+      case 0: chunk_tiles<D, ERASE, WANT_O, 0, NW>(sm, lr, lg, a.scale); break;
+      case 1: chunk_tiles<D, ERASE, WANT_O, 1, NW>(sm, lr, lg, a.scale); break;
+      case 2: chunk_tiles<D, ERASE, WANT_O, 2, NW>(sm, lr, lg, a.scale); break;
+      case 3: chunk_tiles<D, ERASE, WANT_O, 3, NW>(sm, lr, lg, a.scale); break;
+      case 4: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 4, NW>(sm, lr, lg, a.scale); break;
+      case 5: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 5, NW>(sm, lr, lg, a.scale); break;
+      case 6: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 6, NW>(sm, lr, lg, a.scale); break;
+      default: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 7, NW>(sm, lr, lg, a.scale); break;
     }
     __syncthreads();
 
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
         for (int u = 0; u < 2; ++u) {
           const int tt = 2 * tp + u;
           const int t = 16 * tt + lr;
-          const float gt = sm.gam[t];
+          const float gt = a.scale * sm.gam[t];
 #pragma unroll
           for (int it = 0; it < NIT; ++it) O[u][it] *= gt;
 #pragma unroll
@@ -627,7 +627,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
           if (t < nv) {
             const size_t ob = (static_cast<size_t>(c0 + t) * a.h_v + h) * D + w * IW + 4 * lg;
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) store4<TO>(a.o, ob + 16 * it, a.scale * O[u][it]);
+            for (int it = 0; it < NIT; ++it) store4<TO>(a.o, ob + 16 * it, O[u][it]);
           }
         }
       }

@@ -128,6 +128,26 @@ def test_output_dtypes(o_dtype):
     check(c, TOL_BF16, o_dtype=dt, o_tol=5e-4)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_output_scale(d):
+    """o_t = scale * S_t q_t with a non-unit scale (1/sqrt(d), as attention
+    scales queries); fp32 outputs so the scale's effect is not hidden by the
+    final rounding; the state does not depend on it."""
+    import torch
+    import linear_attention_state_anchor_amd as sr
+    c = gdn_case([200, 64, 77], 2, 4, d, "bf16", seed=41, normalize_q=True)
+    scale = d ** -0.5
+    S, o = sr.gdn_replay_state(to_dev(c.q), to_dev(c.k), to_dev(c.v), to_dev(c.alpha),
+                               to_dev(c.beta), to_dev(c.cu_seqlens), None, erase=True,
+                               alpha_is_log=c.alpha_is_log, scale=scale, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Sr, orf = oracle.gdn(c.q, c.k, c.v, c.alpha, c.beta, c.cu_seqlens, c.h_k, c.h_v,
+                         alpha_is_log=c.alpha_is_log, erase=True, scale=scale)
+    es, eo = rel_fro(to_np(S), Sr), rel_fro(to_np(o), orf)
+    print(f"    scale {scale:.4f}: rel S {es:.3e} rel o {eo:.3e}", flush=True)
+    assert es <= TOL_BF16 and eo <= 5e-4, (es, eo)
+
+
 def test_fp16_inputs():
     c = gdn_case([400, 33], 1, 2, 128, "bf16", seed=31, normalize_q=True)
     # the same values as fp16 storage (bf16 -> fp16 is exact here)
