@@ -127,6 +127,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
 __device__ __forceinline__ f16x4 as_f16x4(u16x4 v) { return __builtin_bit_cast(f16x4, v); }
+// 16-byte LDS store at a byte address.
+__device__ __forceinline__ void lds_store16(uint32_t addr, u16x8 v) {
+  *(__attribute__((address_space(3))) u16x8*)(static_cast<uintptr_t>(addr)) = v;
+}
 // 16-byte LDS read at an opaque base plus a compile-time byte offset.
 __device__ __forceinline__ f16x8 lds8_at(uint32_t base, int byte_off) {
   return *(const __attribute__((address_space(3))) f16x8*)(static_cast<uintptr_t>(base + byte_off));
@@ -330,20 +334,26 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
   // offset that does not change between chunks.
   u16x8 pk[NPF], pq[NPF], pv[NPF];
   float pa = 0.0f, pb = 0.0f;
-  auto kq_lane = [&]() { return ((w * kWave + l) / CPR) * static_cast<int>(qk_row) + 8 * ((w * kWave + l) % CPR); };
+  // this thread's 16-byte piece: row (w*64 + l) / CPR, column 8 * ((w*64 + l) % CPR)
+  auto lane_row = [&]() { return (static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) / CPR; };
+  auto lane_col = [&]() { return 8u * ((static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) % CPR); };
+  // byte offsets from a uniform row base: 32-bit and unsigned, so the loads
+  // take the scalar-base + vector-offset form without 64-bit address math
+  auto kq_off = [&]() { return 2u * (lane_row() * static_cast<unsigned>(qk_row) + lane_col()); };
+  auto v_off = [&]() { return 2u * (lane_row() * static_cast<unsigned>(v_row) + lane_col()); };
   auto prefetch_kq = [&](int c0n) {
     const int nvn = min(kC, t_end - c0n);
 #pragma unroll
     for (int e = 0; e < NPF; ++e) {
-      const int row = (w * kWave + l) / CPR + (kThreads / CPR) * e;
+      const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
       const uint16_t* kb = kg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
       pk[e] = u16x8{};
       pq[e] = u16x8{};
       if (row < nvn) {
-        pk[e] = *reinterpret_cast<const u16x8*>(kb + kq_lane());
+        pk[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(kb) + kq_off());
         if (want_o) {
           const uint16_t* qb = qg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
-          pq[e] = *reinterpret_cast<const u16x8*>(qb + kq_lane());
+          pq[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(qb) + kq_off());
         }
       }
     }
@@ -351,9 +361,10 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
       pa = 0.0f;
       pb = 0.0f;
       if (l < nvn) {
-        const size_t gi = static_cast<size_t>(c0n + l) * a.h_v + h;
-        pa = a.alpha[gi];
-        pb = a.beta ? a.beta[gi] : 1.0f;
+        const size_t g0 = static_cast<size_t>(c0n) * a.h_v + h;
+        const unsigned go = 4u * static_cast<unsigned>(l) * static_cast<unsigned>(a.h_v);
+        pa = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.alpha + g0) + go);
+        pb = a.beta ? *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.beta + g0) + go) : 1.0f;
       }
     }
   };
@@ -361,10 +372,10 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     const int nvn = min(kC, t_end - c0n);
 #pragma unroll
     for (int e = 0; e < NPF; ++e) {
-      const int row = (w * kWave + l) / CPR + (kThreads / CPR) * e;
+      const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
       const uint16_t* vb = vg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * v_row;
       pv[e] = u16x8{};
-      if (row < nvn) pv[e] = *reinterpret_cast<const u16x8*>(vb + ((w * kWave + l) / CPR) * static_cast<int>(v_row) + 8 * ((w * kWave + l) % CPR));
+      if (row < nvn) pv[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(vb) + v_off());
     }
   };
   // Converts the prefetched raw K and Q to fp16 in place (V stays raw: it
@@ -418,11 +429,10 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     // ---- stage this chunk: K, Q, V rows (already fp16) and gate scalars --
 #pragma unroll
     for (int e = 0; e < NPF; ++e) {
-      const int item = w * kWave + l + kThreads * e;
-      const int row = item / CPR, ch = item % CPR;
-      *reinterpret_cast<u16x8*>(&sm.k[kidx<D>(row, 8 * ch)]) = pk[e];
-      if (want_o) *reinterpret_cast<u16x8*>(&sm.q[qidx<D>(row, 8 * ch)]) = pq[e];
-      *reinterpret_cast<u16x8*>(&sm.w[row * kWS + 8 * ch]) = pv[e];
+      const unsigned row = lane_row() + (kThreads / CPR) * e, col = lane_col();
+      lds_store16(lds_addr(sm.k) + 2 * (row * ChunkSmem<D>::kKS + col), pk[e]);
+      if (want_o) lds_store16(lds_addr(sm.q) + 2 * (row * ChunkSmem<D>::kQS + col), pq[e]);
+      lds_store16(lds_addr(sm.w) + 2 * (row * kWS + col), pv[e]);
     }
     if (w == 0) {
       sm.gcum[l] = n_g;
@@ -625,9 +635,13 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
             for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(U16[ks][it], pb, O[u][it]);
           }
           if (t < nv) {
-            const size_t ob = (static_cast<size_t>(c0 + t) * a.h_v + h) * D + w * IW + 4 * lg;
+            // uniform base (this chunk, this head) + 32-bit lane offset
+            constexpr unsigned kOB = std::is_same<TO, F32>::value ? 4u : 2u;
+            char* ob0 = static_cast<char*>(a.o) + (static_cast<size_t>(c0) * a.h_v + h) * D * kOB;
+            const unsigned oo = kOB * (static_cast<unsigned>(t) * static_cast<unsigned>(a.h_v) * D +
+                                       static_cast<unsigned>(w * IW + 4 * lg));
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) store4<TO>(a.o, ob + 16 * it, O[u][it]);
+            for (int it = 0; it < NIT; ++it) store4<TO>(ob0 + oo + kOB * 16 * it, 0, O[u][it]);
           }
         }
       }
