@@ -210,6 +210,26 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
   f32x4 acc[5];
 #pragma unroll
   for (int q = 0; q < 5; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // decay / gate factors of this lane's tile elements, formed before the
+  // products (they do not depend on them): masked b_t e^{G_t-G_j} for A (the
+  // diagonal block positive, the others negated for -A), scale e^{G_t-G_j}
+  // for P o QK^T
+  float f[5][4];
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    if (!slot_on(q)) continue;
+    const int col = 16 * slot_tc(q) + lr;
+    const float gcol = sm.gcum[col];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * slot_tr(q) + 4 * lg + r;
+      const float dgam = __expf(sm.gcum[row] - gcol);
+      if (slot_kk(q))
+        f[q][r] = row > col ? (q == 0 ? 1.0f : -1.0f) * sm.beta[row] * dgam : 0.0f;
+      else
+        f[q][r] = row >= col ? scale * dgam : 0.0f;
+    }
+  }
   // this lane's row lr, k-slots 8lg.. of the K and Q tiles
   const uint32_t kl = tr_base(lds_addr(&sm.k[kidx<D>(lr, 8 * lg)]));
   const uint32_t ql = WANT_O ? tr_base(lds_addr(&sm.q[qidx<D>(lr, 8 * lg)])) : 0u;
@@ -235,13 +255,13 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * slot_tr(q) + 4 * lg + r;
-      const float dgam = __expf(sm.gcum[row] - sm.gcum[col]);
+      const float val = f[q][r] * acc[q][r];
       if (q == 0)
-        sm.dg[W * 256 + (4 * lg + r) * 16 + lr] = row > col ? sm.beta[row] * dgam * acc[q][r] : 0.0f;
+        sm.dg[W * 256 + (4 * lg + r) * 16 + lr] = val;
       else if (slot_kk(q))
-        sm.a[row * kAS + kperm(col)] = static_cast<_Float16>(row > col ? -(sm.beta[row] * dgam * acc[q][r]) : 0.0f);
+        sm.a[row * kAS + kperm(col)] = static_cast<_Float16>(val);
       else
-        sm.pqk[row * kPS + kperm(col)] = static_cast<_Float16>(row >= col ? scale * dgam * acc[q][r] : 0.0f);
+        sm.pqk[row * kPS + kperm(col)] = static_cast<_Float16>(val);
     }
   }
   if (kDiag) {
