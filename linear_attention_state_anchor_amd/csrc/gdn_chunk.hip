@@ -6,19 +6,23 @@
 // is evaluated 64 tokens at a time.  Within a chunk (g_t = log a_t,
 // G_t = sum_{s<=t} g_s; exact algebra of the recurrence):
 //     A[t][j] = b_t e^{G_t-G_j} (k_t . k_j), j < t          (strictly lower)
-//     (I + A) [W | U~] = [diag(b e^G) K | diag(b) V]
-//     U  = U~ - W S^T                                         (needs the carry)
+//     (I + A) U = diag(b) V - diag(b e^G) K S^T                (needs the carry)
 //     O  = diag(e^G) Q S^T + (P o Q K^T) U,   P[t][j] = e^{G_t-G_j}, j <= t
 //     S^T <- e^{G_C} S^T + K^T diag(e^{G_C-G}) U
 // Erase-free mode (scalar decay only): A = 0, U = diag(b) V.
 //
 // The triangular system is solved by block forward substitution over 16-row
 // blocks: the four 16x16 diagonal blocks are inverted in fp32 (one wave
-// each), then block row i of [W | U~] is (I + A_ii)^{-1} (R_i - sum_{m<i}
-// A_im Y_m), all on the matrix cores with register-resident operands.
+// each), then block row i of U is (I + A_ii)^{-1} (R_i - sum_{m<i}
+// A_im U_m), R being the right-hand side above, all on the matrix cores with
+// register-resident operands.  Solving for U directly (rather than for the
+// S-independent pair T diag(b e^G) K, T diag(b) V and then combining them
+// with S^T) keeps the solve to each wave's own value columns: no key-side
+// columns, no intermediate tile in LDS and no barrier between the solve and
+// the state products.
 //
 // Work layout: one workgroup of NW waves per (sequence, value head) walks the
-// sequence's chunks in order; wave w owns value columns and key columns
+// sequence's chunks in order; wave w owns value columns
 // [w*D/NW, (w+1)*D/NW).  The transposed state S^T (d_k x d_v, fp32) stays in
 // accumulator registers for the whole sequence.  Accumulator tiles feed later
 // products directly as operands: two vertically adjacent 16x16 tiles hold,
@@ -45,21 +49,26 @@ constexpr int kWaves = 4;
 constexpr int kAS = kC + 8;    // fp16 row stride of -A
 constexpr int kPS = kC + 8;    // fp16 row stride of P o QK^T
 constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
+// s_waitcnt immediate for vmcnt(0) with the other counters unconstrained
+// (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <int D>
 struct ChunkSmem {
-  // Row strides (fp16 elements), chosen from measured LDS bank conflicts:
-  // K is read as 16-byte rows and by transpose reads (conflict-free with 16
-  // elements of padding); Q and V / -W are read as 8-byte rows and written as
-  // 2-byte columns (conflict-free, or nearly, with 8).
-  static constexpr int kKS = D + 16;  // K rows
+  // Row strides (fp16 elements), chosen from measured LDS bank conflicts
+  // (32 banks of 4 bytes, one 128-byte phase per cycle): with 8 elements of
+  // padding the 16-byte row reads of K and Q are conflict-free; the 8-byte
+  // row reads (K S^T, the output product) and the transpose reads meet
+  // 2-way conflicts.  16 elements of padding made the transpose reads
+  // conflict-free but the row reads 2- to 4-way, which measured slower.
+  static constexpr int kKS = D + 8;   // K rows
   static constexpr int kQS = D + 8;   // Q rows
-  static constexpr int kWS = D + 8;   // V / -W rows
+  static constexpr int kWS = D + 8;   // V rows
   // Order: everything read with compile-time offsets lies below 64 KB, so a
   // DS instruction's 16-bit offset field holds the array start and one base
   // register serves many reads; K (last) is read through opaque per-lane
   // bases.  Every array starts on a 256-byte boundary (bank-neutral).
-  float gcum[kC];                    // G_t
+  float gcum[kC];                    // G_t log2(e) (base-2 exponent units)
   float gam[kC];                     // e^{G_t}
   float dec[kC];                     // e^{G_C - G_t}
   float beta[kC];                    // b_t (0 past the end of the sequence)
@@ -69,12 +78,12 @@ struct ChunkSmem {
   _Float16 a[kC * kAS];              // -A (strictly lower off-diagonal blocks)
   _Float16 pqk[kC * kPS];            // scale * P o (Q K^T)
   _Float16 q[kC * kQS];              // Q rows
-  uint16_t w[kC * kWS];              // raw V rows at staging, overwritten by -W (fp16)
+  uint16_t w[kC * kWS];              // raw V rows (input bits)
   _Float16 k[kC * kKS];              // K rows
 };
 
 // Storage position of column c in tiles that are read only as K = 32 MFMA
-// operands (-A, P o QK^T and -W): a K = 32 operand gives lane group g the
+// operands (-A and P o QK^T): a K = 32 operand gives lane group g the
 // k-slots {4g..4g+3, 16+4g..16+4g+3} of each 32-column group, which this
 // order stores next to each other, so one 16-byte read fetches them.
 __device__ __forceinline__ constexpr int kperm(int c) {
@@ -214,20 +223,25 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
   // products (they do not depend on them): masked b_t e^{G_t-G_j} for A (the
   // diagonal block positive, the others negated for -A), scale e^{G_t-G_j}
   // for P o QK^T
+  // The gate values are read unconditionally (four rows per vector read) and
+  // the causal mask applied by selects, so no LDS read sits behind a branch.
   float f[5][4];
 #pragma unroll
   for (int q = 0; q < 5; ++q) {
     if (!slot_on(q)) continue;
     const int col = 16 * slot_tc(q) + lr;
+    const int row0 = 16 * slot_tr(q) + 4 * lg;
     const float gcol = sm.gcum[col];
+    const f32x4 grow = *reinterpret_cast<const f32x4*>(&sm.gcum[row0]);
+    const f32x4 wrow = slot_kk(q) ? *reinterpret_cast<const f32x4*>(&sm.beta[row0])
+                                  : f32x4{scale, scale, scale, scale};
+    const float sgn = (q == 0 || !slot_kk(q)) ? 1.0f : -1.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 16 * slot_tr(q) + 4 * lg + r;
-      const float dgam = __expf(sm.gcum[row] - gcol);
-      if (slot_kk(q))
-        f[q][r] = row > col ? (q == 0 ? 1.0f : -1.0f) * sm.beta[row] * dgam : 0.0f;
-      else
-        f[q][r] = row >= col ? scale * dgam : 0.0f;
+      const int row = row0 + r;
+      const float v = sgn * wrow[r] * __builtin_amdgcn_exp2f(grow[r] - gcol);
+      const bool keep = slot_kk(q) ? row > col : row >= col;
+      f[q][r] = keep ? v : 0.0f;
     }
   }
   // this lane's row lr, k-slots 8lg.. of the K and Q tiles
@@ -267,7 +281,9 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
   if (kDiag) {
     // (I + A_WW)^{-1} by forward substitution in fp32, lane column lr; the
     // block's rows come back from LDS as broadcast reads (this wave wrote
-    // them, so no barrier is needed)
+    // them, so no barrier is needed).  Only one lane group does the work:
+    // a broadcast read returns data to every active lane, so four redundant
+    // groups would quadruple the LDS return traffic.
     const int c = lr;
     const float* ab = &sm.dg[W * 256];
     float x[16];
@@ -299,10 +315,6 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
   constexpr int kWS = ChunkSmem<D>::kWS;
   static_assert(NIT >= 1 && IW % 16 == 0, "D too small");
   static_assert(kC * CPR % kThreads == 0, "staging pieces must divide evenly");
-  // -W is stored in K = 32 operand order only when each wave's columns form
-  // whole 32-column groups (the permutation must not move a wave's -W into
-  // another wave's V columns before that wave has read them)
-  constexpr bool kPermW = IW % 32 == 0;
 
   __shared__ ChunkSmem<D> sm;
 
@@ -337,6 +349,11 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
         const int i = w * IW + 16 * it + lr;
         S[jt][it][r] = a.s0 ? a.s0[sbase + static_cast<size_t>(j) * D + i] : 0.0f;
       }
+  // Retire the initial-state loads here: otherwise the compiler's wait
+  // insertion cannot tell at the loop's first read of S whether they are
+  // done, and waits for every outstanding load there in each chunk (which
+  // would include the next chunk's prefetch).
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // P o QK^T tiles (0,1) and (2,3) are read as zeros by the K = 32 steps of
   // the output product and never written otherwise
@@ -361,26 +378,35 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
   // take the scalar-base + vector-offset form without 64-bit address math
   auto kq_off = [&]() { return 2u * (lane_row() * static_cast<unsigned>(qk_row) + lane_col()); };
   auto v_off = [&]() { return 2u * (lane_row() * static_cast<unsigned>(v_row) + lane_col()); };
-  auto prefetch_kq = [&](int c0n) {
-    const int nvn = min(kC, t_end - c0n);
-#pragma unroll
-    for (int e = 0; e < NPF; ++e) {
-      const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
-      const uint16_t* kb = kg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
-      pk[e] = u16x8{};
-      pq[e] = u16x8{};
-      if (row < nvn) {
-        pk[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(kb) + kq_off());
-        if (want_o) {
-          const uint16_t* qb = qg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
-          pq[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(qb) + kq_off());
-        }
-      }
-    }
+  // One 16-byte piece e of the next chunk's K, Q or V rows per thread (zero
+  // past the end of the sequence), and the next chunk's gates (wave 0).
+  auto pf_k = [&](int e, int c0n) {
+    const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
+    const uint16_t* kb = kg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
+    pk[e] = u16x8{};
+    if (row < t_end - c0n)
+      pk[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(kb) + kq_off());
+  };
+  auto pf_q = [&](int e, int c0n) {
+    if (!want_o) return;
+    const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
+    const uint16_t* qb = qg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
+    pq[e] = u16x8{};
+    if (row < t_end - c0n)
+      pq[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(qb) + kq_off());
+  };
+  auto pf_v = [&](int e, int c0n) {
+    const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
+    const uint16_t* vb = vg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * v_row;
+    pv[e] = u16x8{};
+    if (row < t_end - c0n)
+      pv[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(vb) + v_off());
+  };
+  auto pf_gates = [&](int c0n) {
     if (w == 0) {
       pa = 0.0f;
       pb = 0.0f;
-      if (l < nvn) {
+      if (l < t_end - c0n) {
         const size_t g0 = static_cast<size_t>(c0n) * a.h_v + h;
         const unsigned go = 4u * static_cast<unsigned>(l) * static_cast<unsigned>(a.h_v);
         pa = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.alpha + g0) + go);
@@ -388,15 +414,22 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
       }
     }
   };
-  auto prefetch_v = [&](int c0n) {
-    const int nvn = min(kC, t_end - c0n);
+  // Load slot s of a chunk: K pieces, then Q pieces, then V pieces.  Inside
+  // the chunk loop the slots are issued one or two at a time at fixed points
+  // of the compute (the call sites are compile-time constants after
+  // unrolling), so the CU's vector-memory path never sees all waves' loads
+  // of a chunk at once: a wave whose load cannot be accepted stalls in
+  // order, and a burst of 12 loads per wave cost ~2K cycles per chunk.
+  constexpr int kSlots = 3 * NPF;
+  auto pf_slot = [&](int slot, int c0n) {
+    if (slot < NPF) pf_k(slot, c0n);
+    else if (slot < 2 * NPF) pf_q(slot - NPF, c0n);
+    else pf_v(slot - 2 * NPF, c0n);
+  };
+  auto prefetch_all = [&](int c0n) {
+    pf_gates(c0n);
 #pragma unroll
-    for (int e = 0; e < NPF; ++e) {
-      const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
-      const uint16_t* vb = vg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * v_row;
-      pv[e] = u16x8{};
-      if (row < nvn) pv[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(vb) + v_off());
-    }
+    for (int slot = 0; slot < kSlots; ++slot) pf_slot(slot, c0n);
   };
   // Converts the prefetched raw K and Q to fp16 in place (V stays raw: it
   // only enters fp32 arithmetic) and scans the next
@@ -418,14 +451,13 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
       n_be = l < nvn ? pb : 0.0f;
       gl = wave_inclusive_sum(gl);
       const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), kWave - 1));
-      n_g = gl;
+      n_g = gl * 1.4426950408889634f;  // base-2 units for the tile exponents
       n_eg = __expf(gl);
       n_dec = __expf(gC - gl);
     }
   };
   if (t_begin < t_end) {
-    prefetch_kq(t_begin);
-    prefetch_v(t_begin);
+    prefetch_all(t_begin);
     prepare(t_begin);
   }
 
@@ -463,12 +495,19 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     }
     __syncthreads();
 
-    // the next chunk's K, Q and gates fly while this one computes
+    // the next chunk's gates, K, Q and V fly while this one computes; slot
+    // pfn is the next load to issue
     const bool more = c0 + kC < t_end;
-    if (more) {
-      prefetch_kq(c0 + kC);
-      prefetch_v(c0 + kC);
-    }
+    int pfn = 0;
+    auto pf_next = [&](int n) {
+#pragma unroll
+      for (int i = 0; i < n; ++i) {
+        if (more && pfn < kSlots) pf_slot(pfn, c0 + kC);
+        ++pfn;
+      }
+    };
+    if (more) pf_gates(c0 + kC);
+    pf_next(2);
 
     // ---- A (erase) and P o QK^T: lower-triangular 16x16 tiles -------------
     // Waves 0..3 form the diagonal blocks A_ww and invert I + A_ww (a
@@ -489,47 +528,69 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     // U accumulators: tile (tt, it) = token rows 16tt.., value columns
     // w*IW + 16it..
     f32x4 U[4][NIT];
+    // transpose-read base of this lane in the V tile at this wave's columns
+    const uint32_t xv = tr_base(lds_addr(sm.w) + 2 * (w * IW + trv));
     if (ERASE) {
-      // ---- block forward substitution for [W | U~], this wave's columns --
-      // column tile ct < NIT: W columns w*IW + 16ct (kept as -W in LDS);
-      // ct >= NIT: U~ columns w*IW + 16(ct-NIT) (kept in U).  Earlier block
-      // rows come back as fp16 B operands: W from LDS, U~ from registers.
-      f16x4 Wh[3][NIT];  // earlier block rows of W as fp16 operands
-      // transpose-read bases of this lane in the K and V tiles at this
-      // wave's columns
-      const uint32_t xk = tr_base(lds_addr(sm.k) + 2 * (w * IW + tro));
-      const uint32_t xv = tr_base(lds_addr(sm.w) + 2 * (w * IW + trv));
-      auto yprev = [&](int m, int ct) -> f16x4 {
-        if (ct < NIT) return Wh[m][ct];
-        return to_f16x4(U[m][ct - NIT]);
-      };
+      // ---- right-hand side R = diag(b) V - diag(b e^G) K S^T --------------
+      // K S^T for this wave's value columns, one key k-step at a time: S^T
+      // tiles 2kk and 2kk+1 form the fp16 B operand of k-step kk, K rows the
+      // A operand in the same k order.
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) U[tt][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKJ; ++kk) {
+        SR_SCHED_FENCE();
+        pf_next(1);
+        f16x8 s16[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) s16[it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int t = 16 * tt + lr;
+          const f16x8 kb = cat44(lds4(&sm.k[kidx<D>(t, 32 * kk + 4 * lg)]),
+                                 lds4(&sm.k[kidx<D>(t, 32 * kk + 16 + 4 * lg)]));
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(kb, s16[it], U[tt][it]);
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[16 * tt + 4 * lg]);
+      const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sm.bg[16 * tt + 4 * lg]);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const u16x4 vx = lds_tr4(xv, 2 * (16 * tt * kWS + 16 * it));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float bv = raw_to_f32<TI>(vx[r]) * be4[r];
+          U[tt][it][r] = ERASE ? fmaf(-bg4[r], U[tt][it][r], bv) : bv;
+        }
+      }
+    }
+    tr_keep(xv);
+    if (ERASE) {
+      // ---- block forward substitution (I + A) U = R, this wave's columns --
+      // Block row i: U_i = (I + A_ii)^{-1} (R_i - sum_{m<i} A_im U_m); the
+      // solved rows return as fp16 B operands.
+      f16x4 Yh[3][NIT];
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
-        // X = [diag(b e^G) K | diag(b) V] rows of block bi, this wave's
-        // columns: lane (lr, lg) holds rows 16bi+4lg..+3 of column lr
-        f32x4 X[2 * NIT];
-        const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sm.bg[16 * bi + 4 * lg]);
-        const f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[16 * bi + 4 * lg]);
+        pf_next(1);
+        f32x4 X[NIT];
 #pragma unroll
-        for (int ct = 0; ct < NIT; ++ct) {
-          const f16x4 kx = as_f16x4(lds_tr4(xk, 2 * (16 * bi * ChunkSmem<D>::kKS + 16 * ct)));
-          const u16x4 vx = lds_tr4(xv, 2 * (16 * bi * kWS + 16 * ct));
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            X[ct][r] = static_cast<float>(kx[r]) * bg4[r];
-            X[NIT + ct][r] = raw_to_f32<TI>(vx[r]) * be4[r];
-          }
-        }
+        for (int it = 0; it < NIT; ++it) X[it] = U[bi][it];
         const _Float16* arow = &sm.a[(16 * bi + lr) * kAS];
         if (bi == 1) {
           const f16x4 a4 = lds4(arow + 8 * lg);
 #pragma unroll
-          for (int ct = 0; ct < 2 * NIT; ++ct) X[ct] = mfma16x16x16(a4, yprev(0, ct), X[ct]);
+          for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x16(a4, Yh[0][it], X[it]);
         } else if (bi >= 2) {
           const f16x8 a8 = lds8(arow + 8 * lg);
 #pragma unroll
-          for (int ct = 0; ct < 2 * NIT; ++ct)
-            X[ct] = mfma16x16x32(a8, cat44(yprev(0, ct), yprev(1, ct)), X[ct]);
+          for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x32(a8, cat44(Yh[0][it], Yh[1][it]), X[it]);
           if (bi == 3) {
             // the third term as a K = 32 product with zero upper k-slots:
             // accumulating a 16x16x16 MFMA onto a 16x16x32 result (or the
@@ -539,61 +600,18 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
             const f16x4 z4 = {};
             const f16x8 a8z = cat44(lds4(arow + 32 + 8 * lg), z4);
 #pragma unroll
-            for (int ct = 0; ct < 2 * NIT; ++ct) X[ct] = mfma16x16x32(a8z, cat44(yprev(2, ct), z4), X[ct]);
+            for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x32(a8z, cat44(Yh[2][it], z4), X[it]);
           }
         }
         const f16x4 t4 = lds4(&sm.td[bi * 256 + lr * 16 + 4 * lg]);
 #pragma unroll
-        for (int ct = 0; ct < 2 * NIT; ++ct) {
-          const f32x4 y = mfma16x16x16(t4, to_f16x4(X[ct]), f32x4{0.f, 0.f, 0.f, 0.f});
-          if (ct < NIT) {
-            const int j = w * IW + 16 * ct + lr;
-            const f16x4 yh = to_f16x4(y);
-            if (bi < 3) Wh[bi][ct] = yh;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              sm.w[(16 * bi + 4 * lg + r) * kWS + (kPermW ? kperm(j) : j)] = f16_bits(-yh[r]);
-          } else {
-            U[bi][ct - NIT] = y;
-          }
-        }
-      }
-      tr_keep(xk);
-      tr_keep(xv);
-      __syncthreads();  // -W complete
-    } else {
-      const uint32_t xv = tr_base(lds_addr(sm.w) + 2 * (w * IW + trv));
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[16 * tt + 4 * lg]);
-#pragma unroll
         for (int it = 0; it < NIT; ++it) {
-          const u16x4 vx = lds_tr4(xv, 2 * (16 * tt * kWS + 16 * it));
-#pragma unroll
-          for (int r = 0; r < 4; ++r) U[tt][it][r] = raw_to_f32<TI>(vx[r]) * be4[r];
-        }
-      }
-      tr_keep(xv);
-    }
-
-    // ---- U = U~ - W S^T, one key k-step at a time -------------------------
-    // S^T tiles 2kk and 2kk+1 form the fp16 B operand of k-step kk.
-    if (ERASE) {
-#pragma unroll
-      for (int kk = 0; kk < NKJ; ++kk) {
-        SR_SCHED_FENCE();
-        f16x8 s16[NIT];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) s16[it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const _Float16* wr = reinterpret_cast<const _Float16*>(&sm.w[(16 * tt + lr) * kWS + 32 * kk]);
-          const f16x8 av = kPermW ? lds8(wr + 8 * lg) : cat44(lds4(wr + 4 * lg), lds4(wr + 16 + 4 * lg));
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(av, s16[it], U[tt][it]);
+          U[bi][it] = mfma16x16x16(t4, to_f16x4(X[it]), f32x4{0.f, 0.f, 0.f, 0.f});
+          if (bi < 3) Yh[bi][it] = to_f16x4(U[bi][it]);
         }
       }
     }
+    pf_next(kSlots);  // whatever is left
     // U as fp16 B operands: plain (output) and scaled by e^{G_C-G} (state)
     f16x8 U16[2][NIT], UD[2][NIT];
 #pragma unroll
