@@ -55,13 +55,15 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <int D>
 struct ChunkSmem {
-  // Row strides (fp16 elements), chosen from measured LDS bank conflicts
-  // (32 banks of 4 bytes, one 128-byte phase per cycle): with 8 elements of
-  // padding the 16-byte row reads of K and Q are conflict-free; the 8-byte
-  // row reads (K S^T, the output product) and the transpose reads meet
-  // 2-way conflicts.  16 elements of padding made the transpose reads
-  // conflict-free but the row reads 2- to 4-way, which measured slower.
-  static constexpr int kKS = D + 8;   // K rows
+  // Row strides (fp16 elements), chosen for LDS bank conflicts (32 banks of
+  // 4 bytes, one 128-byte phase per cycle).  Q and V: 8 elements of padding,
+  // so 16-byte row reads of 8 consecutive rows, and V's transpose reads, hit
+  // distinct banks or at most 2-way.  K: 16 elements of padding plus a
+  // swizzle (kswz: rows 4..7 of every 8 exchange their 16-byte column chunks
+  // pairwise), so both its 16-byte row reads and its transpose reads are
+  // conflict-free or 2-way; with a plain 8-element pad the transpose reads
+  // would be 4-way under the state's key order (see kkey).
+  static constexpr int kKS = D + 16;  // K rows
   static constexpr int kQS = D + 8;   // Q rows
   static constexpr int kWS = D + 8;   // V rows
   // Order: everything read with compile-time offsets lies below 64 KB, so a
@@ -88,6 +90,19 @@ struct ChunkSmem {
 // order stores next to each other, so one 16-byte read fetches them.
 __device__ __forceinline__ constexpr int kperm(int c) {
   return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c & 31) >> 4) + (c & 3);
+}
+
+// Column swizzle of K row t (fp16 elements, XORed into the column): rows
+// 4..7 of every 8 exchange their 16-byte column chunks pairwise.
+__device__ __forceinline__ int kswz(int t) { return 8 * ((t >> 2) & 1); }
+
+// Key held by element r of lane group g in state tile jt (rows of S^T).  The
+// state's key order is chosen so that the 8 k-slots of lane group g in a
+// K = 32 operand made of tiles 2m and 2m+1 are the 8 consecutive keys
+// 32m + 8g .. 32m + 8g + 7: the K rows (right-hand side) and Q rows (outputs)
+// that meet the state in a product are then one 16-byte read per lane.
+__device__ __forceinline__ constexpr int kkey(int jt, int g, int r) {
+  return 32 * (jt >> 1) + 8 * g + 4 * (jt & 1) + r;
 }
 
 // element (t, j) of the padded K and Q row tiles
@@ -245,7 +260,8 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
     }
   }
   // this lane's row lr, k-slots 8lg.. of the K and Q tiles
-  const uint32_t kl = tr_base(lds_addr(&sm.k[kidx<D>(lr, 8 * lg)]));
+  // (tile row offsets are multiples of 16, so K's swizzle depends on lr only)
+  const uint32_t kl = tr_base(lds_addr(&sm.k[kidx<D>(lr, (8 * lg) ^ kswz(lr))]));
   const uint32_t ql = WANT_O ? tr_base(lds_addr(&sm.q[qidx<D>(lr, 8 * lg)])) : 0u;
 #pragma unroll
   for (int ks = 0; ks < NKJ; ++ks) {
@@ -334,8 +350,8 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
                               : nullptr;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(h) * D;
 
-  // S^T accumulators: tile (jt, it) = key rows 16jt.., value columns
-  // w*IW + 16it..; lane holds column lr, rows 4lg..4lg+3.
+  // S^T accumulators: tile (jt, it) = 16 key rows, value columns
+  // w*IW + 16it..; lane holds column lr and the keys kkey(jt, lg, 0..3).
   f32x4 S[NJT][NIT];
   int lr = tid % 16, lg = (tid / 16) % 4, l = tid % kWave;
   const size_t sbase = (static_cast<size_t>(n) * a.h_v + h) * D * D;
@@ -345,7 +361,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     for (int it = 0; it < NIT; ++it)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * jt + 4 * lg + r;
+        const int j = kkey(jt, lg, r);
         const int i = w * IW + 16 * it + lr;
         S[jt][it][r] = a.s0 ? a.s0[sbase + static_cast<size_t>(j) * D + i] : 0.0f;
       }
@@ -474,7 +490,9 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
       l = t_ & (kWave - 1);
       lr = t_ & 15;
       lg = (t_ >> 4) & 3;
-      tro = (l >> 2) * ChunkSmem<D>::kKS + 4 * (l & 3);
+      // K transpose reads: token row (l >> 2) of a 16-row block, the 4 keys
+      // kkey(jt, l & 3, 0..3) (8 (l & 3) + a per-tile constant), swizzled
+      tro = (l >> 2) * ChunkSmem<D>::kKS + ((8 * (l & 3)) ^ kswz(l >> 2));
       trv = (l >> 2) * kWS + 4 * (l & 3);
     }
 
@@ -482,7 +500,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 #pragma unroll
     for (int e = 0; e < NPF; ++e) {
       const unsigned row = lane_row() + (kThreads / CPR) * e, col = lane_col();
-      lds_store16(lds_addr(sm.k) + 2 * (row * ChunkSmem<D>::kKS + col), pk[e]);
+      lds_store16(lds_addr(sm.k) + 2 * (row * ChunkSmem<D>::kKS + (col ^ kswz(row))), pk[e]);
       if (want_o) lds_store16(lds_addr(sm.q) + 2 * (row * ChunkSmem<D>::kQS + col), pq[e]);
       lds_store16(lds_addr(sm.w) + 2 * (row * kWS + col), pv[e]);
     }
@@ -549,8 +567,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int t = 16 * tt + lr;
-          const f16x8 kb = cat44(lds4(&sm.k[kidx<D>(t, 32 * kk + 4 * lg)]),
-                                 lds4(&sm.k[kidx<D>(t, 32 * kk + 16 + 4 * lg)]));
+          const f16x8 kb = lds8(&sm.k[kidx<D>(t, (32 * kk + 8 * lg) ^ kswz(t))]);
 #pragma unroll
           for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(kb, s16[it], U[tt][it]);
         }
@@ -651,8 +668,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int t = 16 * (2 * tp + u) + lr;
-            const f16x8 qb = cat44(lds4(&sm.q[qidx<D>(t, 32 * kk + 4 * lg)]),
-                                   lds4(&sm.q[qidx<D>(t, 32 * kk + 16 + 4 * lg)]));
+            const f16x8 qb = lds8(&sm.q[qidx<D>(t, 32 * kk + 8 * lg)]);
 #pragma unroll
             for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(s16[it], qb, O[u][it]);
           }
@@ -696,10 +712,11 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
         for (int it = 0; it < NIT; ++it) S[jt][it] *= gC;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          // K^T rows 16jt.., token k-slots {32ks+4lg.., 32ks+16+4lg..}
+          // K^T rows kkey(jt, ..), token k-slots {32ks+4lg.., 32ks+16+4lg..}
           constexpr int KS = ChunkSmem<D>::kKS;
-          const f16x8 av = cat44(as_f16x4(lds_tr4(sb, 2 * (32 * ks * KS + 16 * jt))),
-                                 as_f16x4(lds_tr4(sb, 2 * ((32 * ks + 16) * KS + 16 * jt))));
+          const int kc = kkey(jt, 0, 0);
+          const f16x8 av = cat44(as_f16x4(lds_tr4(sb, 2 * (32 * ks * KS + kc))),
+                                 as_f16x4(lds_tr4(sb, 2 * ((32 * ks + 16) * KS + kc))));
 #pragma unroll
           for (int it = 0; it < NIT; ++it) S[jt][it] = mfma16x16x32(av, UD[ks][it], S[jt][it]);
         }
@@ -716,7 +733,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     for (int it = 0; it < NIT; ++it)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * jt + 4 * lg + r;
+        const int j = kkey(jt, lg, r);
         const int i = w * IW + 16 * it + lr;
         a.s_out[sbase + static_cast<size_t>(j) * D + i] = S[jt][it][r];
       }
