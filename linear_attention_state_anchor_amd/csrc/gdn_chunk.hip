@@ -6,16 +6,19 @@
 // is evaluated 64 tokens at a time.  Within a chunk (g_t = log a_t,
 // G_t = sum_{s<=t} g_s; exact algebra of the recurrence):
 //     A[t][j] = b_t e^{G_t-G_j} (k_t . k_j), j < t          (strictly lower)
-//     (I + A) U = diag(b) V - diag(b e^G) K S^T                (needs the carry)
+//     (I + A) U = diag(b) (V - diag(e^G) K S^T)                (needs the carry)
 //     O  = diag(e^G) Q S^T + (P o Q K^T) U,   P[t][j] = e^{G_t-G_j}, j <= t
 //     S^T <- e^{G_C} S^T + K^T diag(e^{G_C-G}) U
 // Erase-free mode (scalar decay only): A = 0, U = diag(b) V.
 //
 // The triangular system is solved by block forward substitution over 16-row
-// blocks: the four 16x16 diagonal blocks are inverted in fp32 (one wave
-// each), then block row i of U is (I + A_ii)^{-1} (R_i - sum_{m<i}
-// A_im U_m), R being the right-hand side above, all on the matrix cores with
-// register-resident operands.  Solving for U directly (rather than for the
+// blocks.  With A = diag(b) A~ (A~ without the b_t factor) and
+// R~ = V - diag(e^G) K S^T, block row i reads
+//     U_i = (I + A_ii)^{-1} diag(b_i) (R~_i - sum_{m<i} A~_im U_m):
+// the four 16x16 diagonal blocks are inverted in fp32 (one wave each) and
+// stored with their columns scaled by b, the off-diagonal tiles hold -A~, so
+// neither the right-hand side nor the off-diagonal tiles carry b; all
+// products run on the matrix cores with register-resident operands.  Solving for U directly (rather than for the
 // S-independent pair T diag(b e^G) K, T diag(b) V and then combining them
 // with S^T) keeps the solve to each wave's own value columns: no key-side
 // columns, no intermediate tile in LDS and no barrier between the solve and
@@ -74,7 +77,6 @@ struct ChunkSmem {
   float gam[kC];                     // e^{G_t}
   float dec[kC];                     // e^{G_C - G_t}
   float beta[kC];                    // b_t (0 past the end of the sequence)
-  float bg[kC];                      // b_t e^{G_t}
   _Float16 td[4 * 16 * 16];          // (I + A_bb)^{-1}, row-major per block
   float dg[4 * 16 * 16];             // A_bb, fp32, row-major per block
   _Float16 a[kC * kAS];              // -A (strictly lower off-diagonal blocks)
@@ -235,8 +237,8 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
 #pragma unroll
   for (int q = 0; q < 5; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   // decay / gate factors of this lane's tile elements, formed before the
-  // products (they do not depend on them): masked b_t e^{G_t-G_j} for A (the
-  // diagonal block positive, the others negated for -A), scale e^{G_t-G_j}
+  // products (they do not depend on them): masked b_t e^{G_t-G_j} for the
+  // diagonal A block, -e^{G_t-G_j} for the others (-A~), scale e^{G_t-G_j}
   // for P o QK^T
   // The gate values are read unconditionally (four rows per vector read) and
   // the causal mask applied by selects, so no LDS read sits behind a branch.
@@ -248,8 +250,11 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
     const int row0 = 16 * slot_tr(q) + 4 * lg;
     const float gcol = sm.gcum[col];
     const f32x4 grow = *reinterpret_cast<const f32x4*>(&sm.gcum[row0]);
-    const f32x4 wrow = slot_kk(q) ? *reinterpret_cast<const f32x4*>(&sm.beta[row0])
-                                  : f32x4{scale, scale, scale, scale};
+    // b_t only on the diagonal block (the inverse needs the true A_WW); the
+    // off-diagonal A tiles hold -A~, the P o QK^T tiles carry the scale
+    const f32x4 wrow = q == 0 ? *reinterpret_cast<const f32x4*>(&sm.beta[row0])
+                       : slot_kk(q) ? f32x4{1.0f, 1.0f, 1.0f, 1.0f}
+                                    : f32x4{scale, scale, scale, scale};
     const float sgn = (q == 0 || !slot_kk(q)) ? 1.0f : -1.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -311,8 +316,16 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
       x[r] = t;
     }
     if (lg == 0) {
+      // stored as (I + A_WW)^{-1} diag(b) (column c scaled by b of token
+      // 16W + c); each value pinned in fp32 before its fp16 rounding, so no
+      // template instance fuses the scaling with the conversion
+      const float bc = sm.beta[16 * W + c];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sm.td[W * 256 + r * 16 + c] = static_cast<_Float16>(x[r]);
+      for (int r = 0; r < 16; ++r) {
+        float xr = x[r] * bc;
+        asm volatile("" : "+v"(xr));
+        sm.td[W * 256 + r * 16 + c] = static_cast<_Float16>(xr);
+      }
     }
   }
 }
@@ -509,7 +522,6 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
       sm.gam[l] = n_eg;
       sm.dec[l] = n_dec;
       sm.beta[l] = n_be;
-      sm.bg[l] = n_be * n_eg;
     }
     __syncthreads();
 
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     // transpose-read base of this lane in the V tile at this wave's columns
     const uint32_t xv = tr_base(lds_addr(sm.w) + 2 * (w * IW + trv));
     if (ERASE) {
-      // ---- right-hand side R = diag(b) V - diag(b e^G) K S^T --------------
+      // ---- right-hand side R~ = V - diag(e^G) K S^T ------------------------
       // K S^T for this wave's value columns, one key k-step at a time: S^T
       // tiles 2kk and 2kk+1 form the fp16 B operand of k-step kk, K rows the
       // A operand in the same k order.
@@ -575,23 +587,29 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
+      // erase: R~ = V - e^G (K S^T) (b is applied by the solve); erase-free:
+      // U = diag(b) V
       const f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[16 * tt + 4 * lg]);
-      const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sm.bg[16 * tt + 4 * lg]);
+      const f32x4 ga4 = *reinterpret_cast<const f32x4*>(&sm.gam[16 * tt + 4 * lg]);
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const u16x4 vx = lds_tr4(xv, 2 * (16 * tt * kWS + 16 * it));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float bv = raw_to_f32<TI>(vx[r]) * be4[r];
-          U[tt][it][r] = ERASE ? fmaf(-bg4[r], U[tt][it][r], bv) : bv;
+          const float vv = raw_to_f32<TI>(vx[r]);
+          U[tt][it][r] = ERASE ? fmaf(-ga4[r], U[tt][it][r], vv) : vv * be4[r];
         }
+        // pinned in fp32: the solve rounds it to fp16, and a fused
+        // FMA-with-conversion in some template instances only would make the
+        // state-only and full replays differ in the last bit
+        asm volatile("" : "+v"(U[tt][it]));
       }
     }
     tr_keep(xv);
     if (ERASE) {
-      // ---- block forward substitution (I + A) U = R, this wave's columns --
-      // Block row i: U_i = (I + A_ii)^{-1} (R_i - sum_{m<i} A_im U_m); the
-      // solved rows return as fp16 B operands.
+      // ---- block forward substitution (I + A) U = diag(b) R~, this wave's
+      // columns.  Block row i: U_i = [(I + A_ii)^{-1} diag(b_i)] (R~_i +
+      // sum_{m<i} (-A~_im) U_m); the solved rows return as fp16 B operands.
       f16x4 Yh[3][NIT];
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
