@@ -44,11 +44,12 @@ namespace sr {
 namespace {
 
 constexpr int kC = 64;         // chunk length (tokens)
-// Waves per workgroup (the code also supports 8 at d = 128: 16 value
-// columns per wave; measured slower there, as the register budget of four
-// waves per SIMD forces spills).  Two workgroups share a CU (LDS-bound).
-template <int D>
-constexpr int kWaves = 4;
+// Waves per value head; a workgroup holds HP value heads that share one key
+// head (HP = 2 where the value heads per key head are even: K and Q rows are
+// loaded and staged once and the raw K K^T and Q K^T tiles formed once for
+// both, one workgroup of 8 waves per CU; otherwise HP = 1, two workgroups of
+// 4 waves per CU).
+constexpr int kNW = 4;
 constexpr int kAS = kC + 8;    // fp16 row stride of -A
 constexpr int kPS = kC + 8;    // fp16 row stride of P o QK^T
 constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
@@ -56,7 +57,7 @@ constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
 // (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <int D>
+template <int D, int HP>
 struct ChunkSmem {
   // Row strides (fp16 elements), chosen for LDS bank conflicts (32 banks of
   // 4 bytes, one 128-byte phase per cycle).  Q and V: 8 elements of padding,
@@ -73,16 +74,18 @@ struct ChunkSmem {
   // DS instruction's 16-bit offset field holds the array start and one base
   // register serves many reads; K (last) is read through opaque per-lane
   // bases.  Every array starts on a 256-byte boundary (bank-neutral).
-  float gcum[kC];                    // G_t log2(e) (base-2 exponent units)
-  float gam[kC];                     // e^{G_t}
-  float dec[kC];                     // e^{G_C - G_t}
-  float beta[kC];                    // b_t (0 past the end of the sequence)
-  _Float16 td[4 * 16 * 16];          // (I + A_bb)^{-1}, row-major per block
-  float dg[4 * 16 * 16];             // A_bb, fp32, row-major per block
-  _Float16 a[kC * kAS];              // -A (strictly lower off-diagonal blocks)
-  _Float16 pqk[kC * kPS];            // scale * P o (Q K^T)
+  // Per value head ([HP]): gates, inverse blocks, tiles and V; K and Q are
+  // shared by the heads of the workgroup.
+  float gcum[HP][kC];                // G_t log2(e) (base-2 exponent units)
+  float gam[HP][kC];                 // e^{G_t}
+  float dec[HP][kC];                 // e^{G_C - G_t}
+  float beta[HP][kC];                // b_t (0 past the end of the sequence)
+  _Float16 td[HP][4 * 16 * 16];      // (I + A_bb)^{-1} diag(b), row-major per block
+  float dg[HP][4 * 16 * 16];         // A_bb, fp32, row-major per block
+  _Float16 a[HP][kC * kAS];          // -A~ (strictly lower off-diagonal blocks)
+  _Float16 pqk[HP][kC * kPS];        // scale * P o (Q K^T)
   _Float16 q[kC * kQS];              // Q rows
-  uint16_t w[kC * kWS];              // raw V rows (input bits)
+  uint16_t w[HP][kC * kWS];          // raw V rows (input bits)
   _Float16 k[kC * kKS];              // K rows
 };
 
@@ -110,11 +113,11 @@ __device__ __forceinline__ constexpr int kkey(int jt, int g, int r) {
 // element (t, j) of the padded K and Q row tiles
 template <int D>
 __device__ __forceinline__ int kidx(int t, int j) {
-  return t * ChunkSmem<D>::kKS + j;
+  return t * ChunkSmem<D, 1>::kKS + j;
 }
 template <int D>
 __device__ __forceinline__ int qidx(int t, int j) {
-  return t * ChunkSmem<D>::kQS + j;
+  return t * ChunkSmem<D, 1>::kQS + j;
 }
 
 __device__ __forceinline__ f16x8 lds8(const _Float16* p) {
@@ -203,65 +206,69 @@ __device__ __forceinline__ float raw_to_f32<F16>(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
-// Tile jobs of wave W for one chunk.  Waves 0..3 each form a diagonal block
-// A_WW (erase mode) and invert I + A_WW.  With 4 waves, wave W also takes
-// jobs W, W+4, W+8, W+12 of the list below; with 8 waves, waves 0..3 take
-// one job each (12..15) and waves 4..7 the other twelve, three each.  The job
-// list is fixed at compile time so the whole section is straight-line code
-// with immediate LDS offsets, and the k-steps of all jobs interleave.
+// Tile jobs of wave W for one chunk.  Each wave forms the diagonal block
+// A_bb (erase mode; b = W % 4) of its own head and inverts I + A_bb.  The 16
+// other tiles are shared jobs: with one head, wave W takes jobs W, W+4, W+8,
+// W+12; with two heads (8 waves), wave W takes jobs 2W and 2W+1 and writes
+// each tile once per head (the raw product is the same, the gate factors
+// differ).  The job list is fixed at compile time so the whole section is
+// straight-line code with immediate LDS offsets, and the k-steps of all jobs
+// interleave.
 //   A tile jobs:        (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 //   P o QK^T tile jobs: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-template <int D, bool ERASE, bool WANT_O, int W, int NW>
-__device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, float scale) {
+template <int D, int HP, bool ERASE, bool WANT_O, int W>
+__device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg, float scale) {
   constexpr int NKJ = D / 32;
   constexpr int kJob[16][3] = {{1, 1, 0}, {1, 2, 0}, {1, 2, 1}, {1, 3, 0}, {1, 3, 1}, {1, 3, 2},
                                {0, 0, 0}, {0, 1, 0}, {0, 1, 1}, {0, 2, 0}, {0, 2, 1}, {0, 2, 2},
                                {0, 3, 0}, {0, 3, 1}, {0, 3, 2}, {0, 3, 3}};
-  constexpr bool kDiag = ERASE && W < 4;
-  // slot 0: the diagonal A block; slots 1..4: this wave's jobs (-1: none)
-  auto job = [](int q) constexpr {
-    if (NW == 4) return W + 4 * (q - 1);
-    if (W < 4) return q == 1 ? 12 + W : -1;
-    return q <= 3 ? (W - 4) + 4 * (q - 1) : -1;
-  };
+  constexpr int HW = W / kNW;     // this wave's head
+  constexpr int WQ = W % kNW;     // its diagonal block
+  constexpr bool kDiag = ERASE;
+  constexpr int NS = HP == 1 ? 5 : 3;  // slot 0: diagonal block; then the jobs
+  auto job = [](int q) constexpr { return HP == 1 ? W + 4 * (q - 1) : 2 * W + (q - 1); };
   auto slot_on = [job](int q) constexpr {
     if (q == 0) return kDiag;
-    const int j = job(q);
-    if (j < 0) return false;
-    return kJob[j][0] == 1 ? ERASE : WANT_O;
+    return kJob[job(q)][0] == 1 ? ERASE : WANT_O;
   };
   auto slot_kk = [job](int q) constexpr { return q == 0 || kJob[job(q)][0] == 1; };
-  auto slot_tr = [job](int q) constexpr { return q == 0 ? W : kJob[job(q)][1]; };
-  auto slot_tc = [job](int q) constexpr { return q == 0 ? W : kJob[job(q)][2]; };
-  f32x4 acc[5];
+  auto slot_tr = [job](int q) constexpr { return q == 0 ? WQ : kJob[job(q)][1]; };
+  auto slot_tc = [job](int q) constexpr { return q == 0 ? WQ : kJob[job(q)][2]; };
+  auto slot_h0 = [](int q) constexpr { return q == 0 ? HW : 0; };   // first head written
+  auto slot_nh = [](int q) constexpr { return q == 0 ? 1 : HP; };   // heads written
+  f32x4 acc[NS];
 #pragma unroll
-  for (int q = 0; q < 5; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < NS; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   // decay / gate factors of this lane's tile elements, formed before the
   // products (they do not depend on them): masked b_t e^{G_t-G_j} for the
   // diagonal A block, -e^{G_t-G_j} for the others (-A~), scale e^{G_t-G_j}
-  // for P o QK^T
-  // The gate values are read unconditionally (four rows per vector read) and
-  // the causal mask applied by selects, so no LDS read sits behind a branch.
-  float f[5][4];
+  // for P o QK^T.  The gate values are read unconditionally (four rows per
+  // vector read) and the causal mask applied by selects, so no LDS read sits
+  // behind a branch.
+  float f[NS][HP][4];
 #pragma unroll
-  for (int q = 0; q < 5; ++q) {
+  for (int q = 0; q < NS; ++q) {
     if (!slot_on(q)) continue;
     const int col = 16 * slot_tc(q) + lr;
     const int row0 = 16 * slot_tr(q) + 4 * lg;
-    const float gcol = sm.gcum[col];
-    const f32x4 grow = *reinterpret_cast<const f32x4*>(&sm.gcum[row0]);
-    // b_t only on the diagonal block (the inverse needs the true A_WW); the
-    // off-diagonal A tiles hold -A~, the P o QK^T tiles carry the scale
-    const f32x4 wrow = q == 0 ? *reinterpret_cast<const f32x4*>(&sm.beta[row0])
-                       : slot_kk(q) ? f32x4{1.0f, 1.0f, 1.0f, 1.0f}
-                                    : f32x4{scale, scale, scale, scale};
-    const float sgn = (q == 0 || !slot_kk(q)) ? 1.0f : -1.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + r;
-      const float v = sgn * wrow[r] * __builtin_amdgcn_exp2f(grow[r] - gcol);
-      const bool keep = slot_kk(q) ? row > col : row >= col;
-      f[q][r] = keep ? v : 0.0f;
+    for (int hh = 0; hh < slot_nh(q); ++hh) {
+      const int hd = slot_h0(q) + hh;
+      const float gcol = sm.gcum[hd][col];
+      const f32x4 grow = *reinterpret_cast<const f32x4*>(&sm.gcum[hd][row0]);
+      // b_t only on the diagonal block (the inverse needs the true A_bb); the
+      // off-diagonal A tiles hold -A~, the P o QK^T tiles carry the scale
+      const f32x4 wrow = q == 0 ? *reinterpret_cast<const f32x4*>(&sm.beta[hd][row0])
+                         : slot_kk(q) ? f32x4{1.0f, 1.0f, 1.0f, 1.0f}
+                                      : f32x4{scale, scale, scale, scale};
+      const float sgn = (q == 0 || !slot_kk(q)) ? 1.0f : -1.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + r;
+        const float v = sgn * wrow[r] * __builtin_amdgcn_exp2f(grow[r] - gcol);
+        const bool keep = slot_kk(q) ? row > col : row >= col;
+        f[q][hh][r] = keep ? v : 0.0f;
+      }
     }
   }
   // this lane's row lr, k-slots 8lg.. of the K and Q tiles
@@ -271,7 +278,7 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
 #pragma unroll
   for (int ks = 0; ks < NKJ; ++ks) {
 #pragma unroll
-    for (int q = 0; q < 5; ++q) {
+    for (int q = 0; q < NS; ++q) {
       if (!slot_on(q)) continue;
       const f16x8 av = slot_kk(q) ? lds8_at(kl, 2 * kidx<D>(16 * slot_tr(q), 32 * ks))
                                   : lds8_at(ql, 2 * qidx<D>(16 * slot_tr(q), 32 * ks));
@@ -284,29 +291,33 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
   // epilogues: masked, decay-weighted tiles to LDS (the diagonal A block in
   // fp32 for the inverse)
 #pragma unroll
-  for (int q = 0; q < 5; ++q) {
+  for (int q = 0; q < NS; ++q) {
     if (!slot_on(q)) continue;
     const int col = 16 * slot_tc(q) + lr;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * slot_tr(q) + 4 * lg + r;
-      const float val = f[q][r] * acc[q][r];
-      if (q == 0)
-        sm.dg[W * 256 + (4 * lg + r) * 16 + lr] = val;
-      else if (slot_kk(q))
-        sm.a[row * kAS + kperm(col)] = static_cast<_Float16>(val);
-      else
-        sm.pqk[row * kPS + kperm(col)] = static_cast<_Float16>(val);
+    for (int hh = 0; hh < slot_nh(q); ++hh) {
+      const int hd = slot_h0(q) + hh;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * slot_tr(q) + 4 * lg + r;
+        const float val = f[q][hh][r] * acc[q][r];
+        if (q == 0)
+          sm.dg[HW][WQ * 256 + (4 * lg + r) * 16 + lr] = val;
+        else if (slot_kk(q))
+          sm.a[hd][row * kAS + kperm(col)] = static_cast<_Float16>(val);
+        else
+          sm.pqk[hd][row * kPS + kperm(col)] = static_cast<_Float16>(val);
+      }
     }
   }
   if (kDiag) {
-    // (I + A_WW)^{-1} by forward substitution in fp32, lane column lr; the
+    // (I + A_bb)^{-1} by forward substitution in fp32, lane column lr; the
     // block's rows come back from LDS as broadcast reads (this wave wrote
     // them, so no barrier is needed).  Only one lane group does the work:
     // a broadcast read returns data to every active lane, so four redundant
     // groups would quadruple the LDS return traffic.
     const int c = lr;
-    const float* ab = &sm.dg[W * 256];
+    const float* ab = &sm.dg[HW][WQ * 256];
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -316,52 +327,62 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D>& sm, int lr, int lg, fl
       x[r] = t;
     }
     if (lg == 0) {
-      // stored as (I + A_WW)^{-1} diag(b) (column c scaled by b of token
-      // 16W + c); each value pinned in fp32 before its fp16 rounding, so no
+      // stored as (I + A_bb)^{-1} diag(b) (column c scaled by b of token
+      // 16b + c); each value pinned in fp32 before its fp16 rounding, so no
       // template instance fuses the scaling with the conversion
-      const float bc = sm.beta[16 * W + c];
+      const float bc = sm.beta[HW][16 * WQ + c];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float xr = x[r] * bc;
         asm volatile("" : "+v"(xr));
-        sm.td[W * 256 + r * 16 + c] = static_cast<_Float16>(xr);
+        sm.td[HW][WQ * 256 + r * 16 + c] = static_cast<_Float16>(xr);
       }
     }
   }
 }
 
-template <int D, typename TI, typename TO, bool ERASE, bool WANT_O>
-__global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kernel(GdnArgs a,
-                                                                                  int units_per_xcd) {
-  constexpr int NW = kWaves<D>;
-  constexpr int kThreads = 64 * NW;
-  constexpr int IW = D / NW;      // value (and key) columns per wave
+template <int D, typename TI, typename TO, bool ERASE, bool WANT_O, int HP>
+__global__ __launch_bounds__(64 * kNW * HP, HP == 1 ? 2 : 1) void gdn_chunk_kernel(
+    GdnArgs a, int units_per_xcd) {
+  constexpr int NW = kNW;
+  constexpr int kThreads = 64 * NW * HP;
+  constexpr int IW = D / NW;      // value columns per wave
   constexpr int NIT = IW / 16;    // 16-wide column tiles per wave
   constexpr int NJT = D / 16;     // 16-wide key tiles
   constexpr int NKJ = D / 32;     // K = 32 steps over the key dimension
   constexpr int CPR = D / 8;      // 16-byte chunks per row
   constexpr int NPF = kC * CPR / kThreads;  // 16-byte K (and Q) row pieces per thread
-  constexpr int kWS = ChunkSmem<D>::kWS;
+  constexpr int VCP = CPR * HP;             // 16-byte V pieces per token row (all heads)
+  constexpr int NPFV = kC * VCP / kThreads; // V pieces per thread
+  constexpr int kWS = ChunkSmem<D, HP>::kWS;
   static_assert(NIT >= 1 && IW % 16 == 0, "D too small");
-  static_assert(kC * CPR % kThreads == 0, "staging pieces must divide evenly");
+  static_assert(kC * CPR % kThreads == 0 && kThreads % VCP == 0,
+                "staging pieces must divide evenly");
 
-  __shared__ ChunkSmem<D> sm;
+  __shared__ ChunkSmem<D, HP> sm;
 
-  // XCD-aware numbering: consecutive (sequence, head) units share an XCD.
+  // XCD-aware numbering: consecutive (sequence, head group) units share an
+  // XCD (with one head per workgroup, the value heads of a key head then
+  // read K and Q through one L2).
   const int unit = (blockIdx.x % kXcd) * units_per_xcd + blockIdx.x / kXcd;
-  if (unit >= a.n_seqs * a.h_v) return;  // padding workgroup
-  const int n = unit / a.h_v;
-  const int h = unit % a.h_v;
-  const int g = h / (a.h_v / a.h_k);
+  const int groups = a.h_v / HP;  // head groups per sequence
+  if (unit >= a.n_seqs * groups) return;  // padding workgroup
+  const int n = unit / groups;
+  const int hb = (unit % groups) * HP;    // first value head of the workgroup
+  const int g = hb / (a.h_v / a.h_k);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+  const int hp = w / NW;  // this wave's head within the workgroup
+  const int wq = w % NW;  // this wave within its head
+  const int h = hb + hp;
   constexpr bool want_o = WANT_O;
   const size_t qk_row = static_cast<size_t>(a.h_k) * D;  // elements per token
   const size_t v_row = static_cast<size_t>(a.h_v) * D;
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + static_cast<size_t>(g) * D;
   const uint16_t* qg = want_o ? static_cast<const uint16_t*>(a.q) + static_cast<size_t>(g) * D
                               : nullptr;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(h) * D;
+  // V rows of the workgroup's heads (adjacent in each token row)
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(hb) * D;
 
   // S^T accumulators: tile (jt, it) = 16 key rows, value columns
   // w*IW + 16it..; lane holds column lr and the keys kkey(jt, lg, 0..3).
@@ -375,7 +396,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = kkey(jt, lg, r);
-        const int i = w * IW + 16 * it + lr;
+        const int i = wq * IW + 16 * it + lr;
         S[jt][it][r] = a.s0 ? a.s0[sbase + static_cast<size_t>(j) * D + i] : 0.0f;
       }
   // Retire the initial-state loads here: otherwise the compiler's wait
@@ -386,10 +407,10 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 
   // P o QK^T tiles (0,1) and (2,3) are read as zeros by the K = 32 steps of
   // the output product and never written otherwise
-  for (int e = tid; e < 256; e += kThreads) {
-    const int rr = e / 16, cc = e % 16;
-    sm.pqk[rr * kPS + kperm(16 + cc)] = static_cast<_Float16>(0.0f);
-    sm.pqk[(32 + rr) * kPS + kperm(48 + cc)] = static_cast<_Float16>(0.0f);
+  for (int e = tid; e < 256 * HP; e += kThreads) {
+    const int hh = e / 256, rr = (e % 256) / 16, cc = e % 16;
+    sm.pqk[hh][rr * kPS + kperm(16 + cc)] = static_cast<_Float16>(0.0f);
+    sm.pqk[hh][(32 + rr) * kPS + kperm(48 + cc)] = static_cast<_Float16>(0.0f);
   }
 
   const int t_begin = a.cu[n];
@@ -398,7 +419,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
   // ---- prefetch registers (raw input bits) for the next chunk -------------
   // Addresses are a uniform row base (scalar registers) plus a per-lane
   // offset that does not change between chunks.
-  u16x8 pk[NPF], pq[NPF], pv[NPF];
+  u16x8 pk[NPF], pq[NPF], pv[NPFV];
   float pa = 0.0f, pb = 0.0f;
   // this thread's 16-byte piece: row (w*64 + l) / CPR, column 8 * ((w*64 + l) % CPR)
   auto lane_row = [&]() { return (static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) / CPR; };
@@ -406,7 +427,10 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
   // byte offsets from a uniform row base: 32-bit and unsigned, so the loads
   // take the scalar-base + vector-offset form without 64-bit address math
   auto kq_off = [&]() { return 2u * (lane_row() * static_cast<unsigned>(qk_row) + lane_col()); };
-  auto v_off = [&]() { return 2u * (lane_row() * static_cast<unsigned>(v_row) + lane_col()); };
+  // V: this thread's piece of a token row of all the workgroup's heads
+  auto v_lane_row = [&]() { return (static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) / VCP; };
+  auto v_lane_piece = [&]() { return (static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) % VCP; };
+  auto v_off = [&]() { return 2u * (v_lane_row() * static_cast<unsigned>(v_row) + 8u * v_lane_piece()); };
   // One 16-byte piece e of the next chunk's K, Q or V rows per thread (zero
   // past the end of the sequence), and the next chunk's gates (wave 0).
   auto pf_k = [&](int e, int c0n) {
@@ -425,14 +449,14 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
       pq[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(qb) + kq_off());
   };
   auto pf_v = [&](int e, int c0n) {
-    const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
-    const uint16_t* vb = vg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * v_row;
+    const int row = static_cast<int>(v_lane_row()) + (kThreads / VCP) * e;
+    const uint16_t* vb = vg + static_cast<size_t>(c0n + (kThreads / VCP) * e) * v_row;
     pv[e] = u16x8{};
     if (row < t_end - c0n)
       pv[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(vb) + v_off());
   };
   auto pf_gates = [&](int c0n) {
-    if (w == 0) {
+    if (wq == 0) {
       pa = 0.0f;
       pb = 0.0f;
       if (l < t_end - c0n) {
@@ -449,7 +473,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
   // unrolling), so the CU's vector-memory path never sees all waves' loads
   // of a chunk at once: a wave whose load cannot be accepted stalls in
   // order, and a burst of 12 loads per wave cost ~2K cycles per chunk.
-  constexpr int kSlots = 3 * NPF;
+  constexpr int kSlots = 2 * NPF + NPFV;
   auto pf_slot = [&](int slot, int c0n) {
     if (slot < NPF) pf_k(slot, c0n);
     else if (slot < 2 * NPF) pf_q(slot - NPF, c0n);
@@ -471,7 +495,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
       pk[e] = raw_to_f16x8<TI>(pk[e]);
       if (want_o) pq[e] = raw_to_f16x8<TI>(pq[e]);
     }
-    if (w == 0) {
+    if (wq == 0) {
       float gl = 0.0f;
       if (l < nvn) {
         gl = a.alpha_is_log ? pa : __logf(pa);
@@ -505,7 +529,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
       lg = (t_ >> 4) & 3;
       // K transpose reads: token row (l >> 2) of a 16-row block, the 4 keys
       // kkey(jt, l & 3, 0..3) (8 (l & 3) + a per-tile constant), swizzled
-      tro = (l >> 2) * ChunkSmem<D>::kKS + ((8 * (l & 3)) ^ kswz(l >> 2));
+      tro = (l >> 2) * ChunkSmem<D, HP>::kKS + ((8 * (l & 3)) ^ kswz(l >> 2));
       trv = (l >> 2) * kWS + 4 * (l & 3);
     }
 
@@ -513,15 +537,19 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 #pragma unroll
     for (int e = 0; e < NPF; ++e) {
       const unsigned row = lane_row() + (kThreads / CPR) * e, col = lane_col();
-      lds_store16(lds_addr(sm.k) + 2 * (row * ChunkSmem<D>::kKS + (col ^ kswz(row))), pk[e]);
-      if (want_o) lds_store16(lds_addr(sm.q) + 2 * (row * ChunkSmem<D>::kQS + col), pq[e]);
-      lds_store16(lds_addr(sm.w) + 2 * (row * kWS + col), pv[e]);
+      lds_store16(lds_addr(sm.k) + 2 * (row * ChunkSmem<D, HP>::kKS + (col ^ kswz(row))), pk[e]);
+      if (want_o) lds_store16(lds_addr(sm.q) + 2 * (row * ChunkSmem<D, HP>::kQS + col), pq[e]);
     }
-    if (w == 0) {
-      sm.gcum[l] = n_g;
-      sm.gam[l] = n_eg;
-      sm.dec[l] = n_dec;
-      sm.beta[l] = n_be;
+#pragma unroll
+    for (int e = 0; e < NPFV; ++e) {
+      const unsigned row = v_lane_row() + (kThreads / VCP) * e, cp = v_lane_piece();
+      lds_store16(lds_addr(&sm.w[cp / CPR][0]) + 2 * (row * kWS + 8 * (cp % CPR)), pv[e]);
+    }
+    if (wq == 0) {
+      sm.gcum[hp][l] = n_g;
+      sm.gam[hp][l] = n_eg;
+      sm.dec[hp][l] = n_dec;
+      sm.beta[hp][l] = n_be;
     }
     __syncthreads();
 
@@ -540,18 +568,18 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     pf_next(2);
 
     // ---- A (erase) and P o QK^T: lower-triangular 16x16 tiles -------------
-    // Waves 0..3 form the diagonal blocks A_ww and invert I + A_ww (a
-    // wave-local LDS round trip, no barrier); every wave takes its share of
-    // the off-diagonal A tiles and the P o QK^T tiles.
+    // Every wave forms the diagonal block of its head's rows 16 (w % 4)..
+    // and inverts it (a wave-local LDS round trip, no barrier), and takes its
+    // share of the off-diagonal A tiles and the P o QK^T tiles.
     switch (w) {
-      case 0: chunk_tiles<D, ERASE, WANT_O, 0, NW>(sm, lr, lg, a.scale); break;
-      case 1: chunk_tiles<D, ERASE, WANT_O, 1, NW>(sm, lr, lg, a.scale); break;
-      case 2: chunk_tiles<D, ERASE, WANT_O, 2, NW>(sm, lr, lg, a.scale); break;
-      case 3: chunk_tiles<D, ERASE, WANT_O, 3, NW>(sm, lr, lg, a.scale); break;
-      case 4: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 4, NW>(sm, lr, lg, a.scale); break;
-      case 5: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 5, NW>(sm, lr, lg, a.scale); break;
-      case 6: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 6, NW>(sm, lr, lg, a.scale); break;
-      default: if constexpr (NW == 8) chunk_tiles<D, ERASE, WANT_O, 7, NW>(sm, lr, lg, a.scale); break;
+      case 0: chunk_tiles<D, HP, ERASE, WANT_O, 0>(sm, lr, lg, a.scale); break;
+      case 1: chunk_tiles<D, HP, ERASE, WANT_O, 1>(sm, lr, lg, a.scale); break;
+      case 2: chunk_tiles<D, HP, ERASE, WANT_O, 2>(sm, lr, lg, a.scale); break;
+      case 3: chunk_tiles<D, HP, ERASE, WANT_O, 3>(sm, lr, lg, a.scale); break;
+      case 4: if constexpr (HP == 2) chunk_tiles<D, HP, ERASE, WANT_O, 4>(sm, lr, lg, a.scale); break;
+      case 5: if constexpr (HP == 2) chunk_tiles<D, HP, ERASE, WANT_O, 5>(sm, lr, lg, a.scale); break;
+      case 6: if constexpr (HP == 2) chunk_tiles<D, HP, ERASE, WANT_O, 6>(sm, lr, lg, a.scale); break;
+      default: if constexpr (HP == 2) chunk_tiles<D, HP, ERASE, WANT_O, 7>(sm, lr, lg, a.scale); break;
     }
     __syncthreads();
 
@@ -559,7 +587,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     // w*IW + 16it..
     f32x4 U[4][NIT];
     // transpose-read base of this lane in the V tile at this wave's columns
-    const uint32_t xv = tr_base(lds_addr(sm.w) + 2 * (w * IW + trv));
+    const uint32_t xv = tr_base(lds_addr(&sm.w[hp][0]) + 2 * (wq * IW + trv));
     if (ERASE) {
       // ---- right-hand side R~ = V - diag(e^G) K S^T ------------------------
       // K S^T for this wave's value columns, one key k-step at a time: S^T
@@ -589,8 +617,8 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
     for (int tt = 0; tt < 4; ++tt) {
       // erase: R~ = V - e^G (K S^T) (b is applied by the solve); erase-free:
       // U = diag(b) V
-      const f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[16 * tt + 4 * lg]);
-      const f32x4 ga4 = *reinterpret_cast<const f32x4*>(&sm.gam[16 * tt + 4 * lg]);
+      const f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[hp][16 * tt + 4 * lg]);
+      const f32x4 ga4 = *reinterpret_cast<const f32x4*>(&sm.gam[hp][16 * tt + 4 * lg]);
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const u16x4 vx = lds_tr4(xv, 2 * (16 * tt * kWS + 16 * it));
@@ -617,7 +645,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
         f32x4 X[NIT];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) X[it] = U[bi][it];
-        const _Float16* arow = &sm.a[(16 * bi + lr) * kAS];
+        const _Float16* arow = &sm.a[hp][(16 * bi + lr) * kAS];
         if (bi == 1) {
           const f16x4 a4 = lds4(arow + 8 * lg);
 #pragma unroll
@@ -638,7 +666,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
             for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x32(a8z, cat44(Yh[2][it], z4), X[it]);
           }
         }
-        const f16x4 t4 = lds4(&sm.td[bi * 256 + lr * 16 + 4 * lg]);
+        const f16x4 t4 = lds4(&sm.td[hp][bi * 256 + lr * 16 + 4 * lg]);
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           U[bi][it] = mfma16x16x16(t4, to_f16x4(X[it]), f32x4{0.f, 0.f, 0.f, 0.f});
@@ -657,8 +685,8 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
         if (want_o) U16[ks][it] = to_f16x8(lo, hi);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          lo[r] *= sm.dec[32 * ks + 4 * lg + r];
-          hi[r] *= sm.dec[32 * ks + 16 + 4 * lg + r];
+          lo[r] *= sm.dec[hp][32 * ks + 4 * lg + r];
+          hi[r] *= sm.dec[hp][32 * ks + 16 + 4 * lg + r];
         }
         UD[ks][it] = to_f16x8(lo, hi);
         // materialise the fp16 copies here so the fp32 U dies now instead of
@@ -695,13 +723,13 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
         for (int u = 0; u < 2; ++u) {
           const int tt = 2 * tp + u;
           const int t = 16 * tt + lr;
-          const float gt = a.scale * sm.gam[t];
+          const float gt = a.scale * sm.gam[hp][t];
 #pragma unroll
           for (int it = 0; it < NIT; ++it) O[u][it] *= gt;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             if (32 * ks > 16 * tt + 15) continue;  // P o QK^T is lower triangular
-            const _Float16* pr = &sm.pqk[t * kPS + 32 * ks];
+            const _Float16* pr = &sm.pqk[hp][t * kPS + 32 * ks];
             const f16x8 pb = lds8(pr + 8 * lg);
 #pragma unroll
             for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(U16[ks][it], pb, O[u][it]);
@@ -711,7 +739,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
             constexpr unsigned kOB = std::is_same<TO, F32>::value ? 4u : 2u;
             char* ob0 = static_cast<char*>(a.o) + (static_cast<size_t>(c0) * a.h_v + h) * D * kOB;
             const unsigned oo = kOB * (static_cast<unsigned>(t) * static_cast<unsigned>(a.h_v) * D +
-                                       static_cast<unsigned>(w * IW + 4 * lg));
+                                       static_cast<unsigned>(wq * IW + 4 * lg));
 #pragma unroll
             for (int it = 0; it < NIT; ++it) store4<TO>(ob0 + oo + kOB * 16 * it, 0, O[u][it]);
           }
@@ -721,7 +749,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 
     // ---- S^T <- e^{G_C} S^T + K^T diag(e^{G_C-G}) U -----------------------
     {
-      const float gC = sm.gam[kC - 1];
+      const float gC = sm.gam[hp][kC - 1];
       const uint32_t sb = tr_base(lds_addr(sm.k) + 2 * tro);
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) {
@@ -731,7 +759,7 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           // K^T rows kkey(jt, ..), token k-slots {32ks+4lg.., 32ks+16+4lg..}
-          constexpr int KS = ChunkSmem<D>::kKS;
+          constexpr int KS = ChunkSmem<D, HP>::kKS;
           const int kc = kkey(jt, 0, 0);
           const f16x8 av = cat44(as_f16x4(lds_tr4(sb, 2 * (32 * ks * KS + kc))),
                                  as_f16x4(lds_tr4(sb, 2 * ((32 * ks + 16) * KS + kc))));
@@ -752,26 +780,33 @@ __global__ __launch_bounds__(64 * kWaves<D>, kWaves<D> / 2) void gdn_chunk_kerne
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = kkey(jt, lg, r);
-        const int i = w * IW + 16 * it + lr;
+        const int i = wq * IW + 16 * it + lr;
         a.s_out[sbase + static_cast<size_t>(j) * D + i] = S[jt][it][r];
       }
 }
 
-template <int D, typename TI, typename TO>
-hipError_t launch3(const GdnArgs& a, hipStream_t s) {
-  const int units = a.n_seqs * a.h_v;
+template <int D, typename TI, typename TO, int HP>
+hipError_t launch4(const GdnArgs& a, hipStream_t s) {
+  const int units = a.n_seqs * (a.h_v / HP);
   const int per_xcd = (units + kXcd - 1) / kXcd;
-  dim3 grid(per_xcd * kXcd), block(64 * kWaves<D>);
+  dim3 grid(per_xcd * kXcd), block(64 * kNW * HP);
   const bool o = a.o != nullptr;
   if (a.erase && o)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true, HP>), grid, block, 0, s, a, per_xcd);
   else if (a.erase)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, false>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, false, HP>), grid, block, 0, s, a, per_xcd);
   else if (o)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, true>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, true, HP>), grid, block, 0, s, a, per_xcd);
   else
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, false>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, false, HP>), grid, block, 0, s, a, per_xcd);
   return hipGetLastError();
+}
+
+// Two value heads per workgroup where the value heads of a key head pair up
+// (their K and Q are then loaded, staged and multiplied once).
+template <int D, typename TI, typename TO>
+hipError_t launch3(const GdnArgs& a, hipStream_t s) {
+  return (a.h_v / a.h_k) % 2 == 0 ? launch4<D, TI, TO, 2>(a, s) : launch4<D, TI, TO, 1>(a, s);
 }
 
 template <int D, typename TI>
