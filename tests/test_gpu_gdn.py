@@ -81,15 +81,14 @@ def test_gdn_bf16_small():
 PAIR_LENS = [0, 1, 63, 64, 65, 127, 128, 129, 200, 17, 3, 90, 150, 64, 31, 70]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d,hk", [(64, 16), (128, 16), (128, 8)])
 @pytest.mark.parametrize("erase", [True, False])
-def test_value_head_pairs(d, erase):
-    """16 ragged sequences x 32 value heads sharing 16 key heads: 512
-    (sequence, head) chains, enough for the launch to put the two value
-    heads of a key head in one workgroup.  Full parity of states and outputs
-    (with an initial state), and the state-only run equals the full run bit
-    for bit."""
-    c = gdn_case(PAIR_LENS, 16, 32, d, "bf16", seed=31 + d + int(erase), normalize_q=True,
+def test_value_head_pairs(d, hk, erase):
+    """16 ragged sequences x 32 value heads sharing 16 (or 8) key heads: 512
+    (sequence, head) chains, enough for the launch to put two value heads of
+    a key head in one workgroup.  Full parity of states and outputs (with an
+    initial state), and the state-only run equals the full run bit for bit."""
+    c = gdn_case(PAIR_LENS, hk, 32, d, "bf16", seed=31 + d + hk + int(erase), normalize_q=True,
                  erase=erase, initial_state=True)
     S, _, _, _ = check(c, TOL_BF16)
     S2, o2 = gpu_run(c, want_o=False)
