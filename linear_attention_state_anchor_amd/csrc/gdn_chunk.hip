@@ -44,12 +44,15 @@ namespace sr {
 namespace {
 
 constexpr int kC = 64;         // chunk length (tokens)
-// Waves per value head; a workgroup holds HP value heads that share one key
-// head (HP = 2 where the value heads per key head are even: K and Q rows are
-// loaded and staged once and the raw K K^T and Q K^T tiles formed once for
-// both, one workgroup of 8 waves per CU; otherwise HP = 1, two workgroups of
-// 4 waves per CU).
-constexpr int kNW = 4;
+// A workgroup holds HP value heads that share one key head, with NW waves
+// per head (HP x NW = 4 or 8 waves):
+//  * HP = 2, NW = 4 where the value heads per key head are even and there
+//    are at least two (sequence, head) chains per CU: K and Q rows are
+//    loaded and staged once and the raw K K^T / Q K^T tiles formed once for
+//    both heads; one workgroup of 8 waves per CU;
+//  * HP = 1, NW = 8 for at most one chain per CU: 16 value columns per
+//    wave, two waves per SIMD instead of one;
+//  * HP = 1, NW = 4 otherwise: two workgroups of 4 waves per CU.
 constexpr int kAS = kC + 8;    // fp16 row stride of -A
 constexpr int kPS = kC + 8;    // fp16 row stride of P o QK^T
 constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
@@ -206,27 +209,28 @@ __device__ __forceinline__ float raw_to_f32<F16>(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
-// Tile jobs of wave W for one chunk.  Each wave forms the diagonal block
-// A_bb (erase mode; b = W % 4) of its own head and inverts I + A_bb.  The 16
-// other tiles are shared jobs: with one head, wave W takes jobs W, W+4, W+8,
-// W+12; with two heads (8 waves), wave W takes jobs 2W and 2W+1 and writes
-// each tile once per head (the raw product is the same, the gate factors
+// Tile jobs of wave W for one chunk.  Waves 0..3 of each head form the
+// diagonal blocks A_bb (erase mode; b = the wave within the head) and invert
+// I + A_bb.  The 16 other tiles are shared jobs: with 4 waves, wave W takes
+// jobs W, W+4, W+8, W+12; with 8 waves, jobs 2W and 2W+1, each written once
+// per head of the workgroup (the raw product is the same, the gate factors
 // differ).  The job list is fixed at compile time so the whole section is
 // straight-line code with immediate LDS offsets, and the k-steps of all jobs
 // interleave.
 //   A tile jobs:        (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 //   P o QK^T tile jobs: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-template <int D, int HP, bool ERASE, bool WANT_O, int W>
+template <int D, int HP, int NW, bool ERASE, bool WANT_O, int W>
 __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg, float scale) {
   constexpr int NKJ = D / 32;
   constexpr int kJob[16][3] = {{1, 1, 0}, {1, 2, 0}, {1, 2, 1}, {1, 3, 0}, {1, 3, 1}, {1, 3, 2},
                                {0, 0, 0}, {0, 1, 0}, {0, 1, 1}, {0, 2, 0}, {0, 2, 1}, {0, 2, 2},
                                {0, 3, 0}, {0, 3, 1}, {0, 3, 2}, {0, 3, 3}};
-  constexpr int HW = W / kNW;     // this wave's head
-  constexpr int WQ = W % kNW;     // its diagonal block
-  constexpr bool kDiag = ERASE;
-  constexpr int NS = HP == 1 ? 5 : 3;  // slot 0: diagonal block; then the jobs
-  auto job = [](int q) constexpr { return HP == 1 ? W + 4 * (q - 1) : 2 * W + (q - 1); };
+  constexpr int NWT = NW * HP;    // waves of the workgroup (4 or 8)
+  constexpr int HW = W / NW;      // this wave's head
+  constexpr int WQ = W % NW;      // its diagonal block (waves 0..3 of a head)
+  constexpr bool kDiag = ERASE && WQ < 4;
+  constexpr int NS = NWT == 4 ? 5 : 3;  // slot 0: diagonal block; then the jobs
+  auto job = [](int q) constexpr { return NWT == 4 ? W + 4 * (q - 1) : 2 * W + (q - 1); };
   auto slot_on = [job](int q) constexpr {
     if (q == 0) return kDiag;
     return kJob[job(q)][0] == 1 ? ERASE : WANT_O;
@@ -341,10 +345,9 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
   }
 }
 
-template <int D, typename TI, typename TO, bool ERASE, bool WANT_O, int HP>
-__global__ __launch_bounds__(64 * kNW * HP, HP == 1 ? 2 : 1) void gdn_chunk_kernel(
+template <int D, typename TI, typename TO, bool ERASE, bool WANT_O, int HP, int NW>
+__global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_kernel(
     GdnArgs a, int units_per_xcd) {
-  constexpr int NW = kNW;
   constexpr int kThreads = 64 * NW * HP;
   constexpr int IW = D / NW;      // value columns per wave
   constexpr int NIT = IW / 16;    // 16-wide column tiles per wave
@@ -572,14 +575,14 @@ __global__ __launch_bounds__(64 * kNW * HP, HP == 1 ? 2 : 1) void gdn_chunk_kern
     // and inverts it (a wave-local LDS round trip, no barrier), and takes its
     // share of the off-diagonal A tiles and the P o QK^T tiles.
     switch (w) {
-      case 0: chunk_tiles<D, HP, ERASE, WANT_O, 0>(sm, lr, lg, a.scale); break;
-      case 1: chunk_tiles<D, HP, ERASE, WANT_O, 1>(sm, lr, lg, a.scale); break;
-      case 2: chunk_tiles<D, HP, ERASE, WANT_O, 2>(sm, lr, lg, a.scale); break;
-      case 3: chunk_tiles<D, HP, ERASE, WANT_O, 3>(sm, lr, lg, a.scale); break;
-      case 4: if constexpr (HP == 2) chunk_tiles<D, HP, ERASE, WANT_O, 4>(sm, lr, lg, a.scale); break;
-      case 5: if constexpr (HP == 2) chunk_tiles<D, HP, ERASE, WANT_O, 5>(sm, lr, lg, a.scale); break;
-      case 6: if constexpr (HP == 2) chunk_tiles<D, HP, ERASE, WANT_O, 6>(sm, lr, lg, a.scale); break;
-      default: if constexpr (HP == 2) chunk_tiles<D, HP, ERASE, WANT_O, 7>(sm, lr, lg, a.scale); break;
+      case 0: chunk_tiles<D, HP, NW, ERASE, WANT_O, 0>(sm, lr, lg, a.scale); break;
+      case 1: chunk_tiles<D, HP, NW, ERASE, WANT_O, 1>(sm, lr, lg, a.scale); break;
+      case 2: chunk_tiles<D, HP, NW, ERASE, WANT_O, 2>(sm, lr, lg, a.scale); break;
+      case 3: chunk_tiles<D, HP, NW, ERASE, WANT_O, 3>(sm, lr, lg, a.scale); break;
+      case 4: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 4>(sm, lr, lg, a.scale); break;
+      case 5: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 5>(sm, lr, lg, a.scale); break;
+      case 6: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 6>(sm, lr, lg, a.scale); break;
+      default: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 7>(sm, lr, lg, a.scale); break;
     }
     __syncthreads();
 
@@ -785,33 +788,37 @@ __global__ __launch_bounds__(64 * kNW * HP, HP == 1 ? 2 : 1) void gdn_chunk_kern
       }
 }
 
-template <int D, typename TI, typename TO, int HP>
+template <int D, typename TI, typename TO, int HP, int NW>
 hipError_t launch4(const GdnArgs& a, hipStream_t s) {
   const int units = a.n_seqs * (a.h_v / HP);
   const int per_xcd = (units + kXcd - 1) / kXcd;
-  dim3 grid(per_xcd * kXcd), block(64 * kNW * HP);
+  dim3 grid(per_xcd * kXcd), block(64 * NW * HP);
   const bool o = a.o != nullptr;
   if (a.erase && o)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true, HP>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true, HP, NW>), grid, block, 0, s, a, per_xcd);
   else if (a.erase)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, false, HP>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, false, HP, NW>), grid, block, 0, s, a, per_xcd);
   else if (o)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, true, HP>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, true, HP, NW>), grid, block, 0, s, a, per_xcd);
   else
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, false, HP>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, false, HP, NW>), grid, block, 0, s, a, per_xcd);
   return hipGetLastError();
 }
 
-// Two value heads per workgroup where the value heads of a key head pair up
-// (their K and Q are then loaded, staged and multiplied once) and there are
-// at least two (sequence, value head) chains per compute unit.  With fewer
-// chains the one-head layout keeps more CUs busy: for 4 x 32 chains it
-// measured 141 us against 184 us for the pair layout.
+// Launch shape by the number of (sequence, value head) chains: two value
+// heads per workgroup where the value heads of a key head pair up and there
+// are at least two chains per compute unit; 8 waves on one head for at most
+// one chain per CU; otherwise one head of 4 waves.  (For 4 x 32 chains the
+// pair layout measured 184 us against 141 us for one head of 4 waves.)
 constexpr int kGfx950Cus = 256;  // compute units of the gfx950 parts (MI350X, MI355X)
 template <int D, typename TI, typename TO>
 hipError_t launch3(const GdnArgs& a, hipStream_t s) {
-  const bool pair = (a.h_v / a.h_k) % 2 == 0 && a.n_seqs * a.h_v >= 2 * kGfx950Cus;
-  return pair ? launch4<D, TI, TO, 2>(a, s) : launch4<D, TI, TO, 1>(a, s);
+  const int chains = a.n_seqs * a.h_v;
+  if ((a.h_v / a.h_k) % 2 == 0 && chains >= 2 * kGfx950Cus) return launch4<D, TI, TO, 2, 4>(a, s);
+  if constexpr (D == 128) {  // 16 value columns per wave (d = 64 would leave 8)
+    if (chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 8>(a, s);
+  }
+  return launch4<D, TI, TO, 1, 4>(a, s);
 }
 
 template <int D, typename TI>

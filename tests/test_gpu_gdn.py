@@ -96,6 +96,23 @@ def test_value_head_pairs(d, hk, erase):
     np.testing.assert_array_equal(S, S2)
 
 
+@pytest.mark.parametrize("n_seqs,hk,hv", [(16, 32, 32), (12, 16, 32), (4, 16, 32)])
+@pytest.mark.parametrize("erase", [True, False])
+def test_launch_shapes(n_seqs, hk, hv, erase):
+    """The launch picks its workgroup shape from the number of (sequence,
+    value head) chains: 512 chains with one value head per key head and 384
+    chains take one head of 4 waves per workgroup, 128 chains one head of 8
+    waves (pairs of heads are covered above).  Full parity with ragged
+    lengths and an initial state, and state-only equals the full run."""
+    lens = (PAIR_LENS * 2)[:n_seqs]
+    c = gdn_case(lens, hk, hv, 128, "bf16", seed=7 * n_seqs + hk + int(erase), normalize_q=True,
+                 erase=erase, initial_state=True)
+    S, _, _, _ = check(c, TOL_BF16)
+    S2, o2 = gpu_run(c, want_o=False)
+    assert o2 is None
+    np.testing.assert_array_equal(S, S2)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("erase", [True, False])
 @pytest.mark.parametrize("hk,hv", [(1, 1), (1, 2), (2, 4)])
