@@ -589,6 +589,13 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
     // U accumulators: tile (tt, it) = token rows 16tt.., value columns
     // w*IW + 16it..
     f32x4 U[4][NIT];
+    // fp16 copy of the state (B operand of K S^T, A operand of the outputs),
+    // converted once per chunk
+    f16x8 S16[NKJ][NIT];
+#pragma unroll
+    for (int kk = 0; kk < NKJ; ++kk)
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) S16[kk][it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
     // transpose-read base of this lane in the V tile at this wave's columns
     const uint32_t xv = tr_base(lds_addr(&sm.w[hp][0]) + 2 * (wq * IW + trv));
     if (ERASE) {
@@ -604,15 +611,12 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
       for (int kk = 0; kk < NKJ; ++kk) {
         SR_SCHED_FENCE();
         pf_next(1);
-        f16x8 s16[NIT];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) s16[it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int t = 16 * tt + lr;
           const f16x8 kb = lds8(&sm.k[kidx<D>(t, (32 * kk + 8 * lg) ^ kswz(t))]);
 #pragma unroll
-          for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(kb, s16[it], U[tt][it]);
+          for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(kb, S16[kk][it], U[tt][it]);
         }
       }
     }
@@ -711,15 +715,12 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
           for (int it = 0; it < NIT; ++it) O[u][it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKJ; ++kk) {
-          f16x8 s16[NIT];
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) s16[it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int t = 16 * (2 * tp + u) + lr;
             const f16x8 qb = lds8(&sm.q[qidx<D>(t, 32 * kk + 8 * lg)]);
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(s16[it], qb, O[u][it]);
+            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(S16[kk][it], qb, O[u][it]);
           }
         }
 #pragma unroll
