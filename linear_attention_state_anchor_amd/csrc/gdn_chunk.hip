@@ -18,24 +18,27 @@
 // the four 16x16 diagonal blocks are inverted in fp32 (one wave each) and
 // stored with their columns scaled by b, the off-diagonal tiles hold -A~, so
 // neither the right-hand side nor the off-diagonal tiles carry b; all
-// products run on the matrix cores with register-resident operands.  Solving for U directly (rather than for the
-// S-independent pair T diag(b e^G) K, T diag(b) V and then combining them
-// with S^T) keeps the solve to each wave's own value columns: no key-side
-// columns, no intermediate tile in LDS and no barrier between the solve and
-// the state products.
+// products run on the matrix cores with register-resident operands.
+// Solving for U directly (rather than for the S-independent pair
+// T diag(b e^G) K, T diag(b) V and then combining them with S^T) keeps the
+// solve to each wave's own value columns: no key-side columns, no
+// intermediate tile in LDS and no barrier between the solve and the state
+// products.
 //
-// Work layout: one workgroup of NW waves per (sequence, value head) walks the
-// sequence's chunks in order; wave w owns value columns
-// [w*D/NW, (w+1)*D/NW).  The transposed state S^T (d_k x d_v, fp32) stays in
-// accumulator registers for the whole sequence.  Accumulator tiles feed later
-// products directly as operands: two vertically adjacent 16x16 tiles hold,
-// per lane, the k-slots {4g..4g+3, 16+4g..16+4g+3} (g = lane/16) of a K = 32
-// operand, and the other operand is read from LDS in the same k order.
-// Operands are fp16 (bf16 inputs convert exactly); accumulation and the
-// state are fp32.  The next chunk's K, Q and V are prefetched into registers
-// while the current chunk computes, so each chunk has a single staging
-// barrier.  Workgroups are numbered so that the value heads sharing a key
-// head run on the same XCD (shared L2 for their K and Q).
+// Work layout: a workgroup holds HP value heads that share a key head, NW
+// waves per head, and walks one sequence's chunks in order; wave w of a head
+// owns value columns [w*D/NW, (w+1)*D/NW) (the launch picks HP and NW from
+// the number of (sequence, head) chains).  The transposed state S^T
+// (d_k x d_v, fp32) stays in accumulator registers for the whole sequence.
+// Accumulator tiles feed later products directly as operands: two
+// vertically adjacent 16x16 tiles hold, per lane, the k-slots of a K = 32
+// operand (see kkey), and the other operand is read from LDS in the same k
+// order.  Operands are fp16 (bf16 inputs convert exactly); accumulation and
+// the state are fp32.  The next chunk's K, Q and V are prefetched into
+// registers while the current chunk computes, so each chunk has a single
+// staging barrier.  Workgroups are numbered so that consecutive head groups
+// of a sequence run on the same XCD (with one head per workgroup, the value
+// heads sharing a key head then read K and Q through one L2).
 #include "sr_common.hpp"
 #include "sr_internal.hpp"
 
