@@ -72,9 +72,22 @@ def read_traffic(bytes_alg):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, budget_s=20.0):
     """Time the fp64 oracle (as it stands) on whole sequences of the same
-    workload, as many as fit about budget_s of host time."""
+    workload, as many as fit about budget_s of host time on all host threads,
+    and on one sequence with a single thread.  Returns (baseline entry,
+    sequences timed, oracle final states, oracle outputs) -- the outputs let
+    the benchmarked launch be checked against the oracle."""
     import numpy as np
     import oracle
     from replay_inputs import gdn_case
@@ -90,24 +103,53 @@ def cpu_baseline(case, budget_s=20.0):
         c.alpha_is_log = case.alpha_is_log
         return c
 
-    def run(c):
+    def run(c, threads=0):
         t0 = time.perf_counter()
-        oracle.gdn(c.q, c.k, c.v, c.alpha, c.beta, c.cu_seqlens, c.h_k, c.h_v,
-                   alpha_is_log=c.alpha_is_log, erase=c.erase)
-        return time.perf_counter() - t0
+        S, o = oracle.gdn(c.q, c.k, c.v, c.alpha, c.beta, c.cu_seqlens, c.h_k, c.h_v,
+                          alpha_is_log=c.alpha_is_log, erase=c.erase, n_threads=threads)
+        return time.perf_counter() - t0, S, o
 
     threads = oracle.max_threads()
     first = sub([0])
-    t1 = run(first)
+    t1, _, _ = run(first)
     n = int(max(1, min(case.n_seqs, budget_s // max(t1, 1e-3))))
     seqs = list(range(n))
     c = sub(seqs)
-    t = run(c)
+    t, S, o = run(c)
+    t_one, _, _ = run(first, threads=1)
     toks = c.total_tokens
-    return {"value": toks / t, "unit": "replayed tokens/s per GDN layer", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} of {case.n_seqs} sequences ({toks} tokens, all {case.h_v} value "
-                      f"heads), fp64 token loop, {t:.2f} s"}
+    entry = {"value": toks / t, "unit": "replayed tokens/s per GDN layer", "cores": threads,
+             "kind": "oracle", "cpu_model": cpu_model(),
+             "one_core_value": first.total_tokens / t_one,
+             "sample": f"{n} of {case.n_seqs} sequences ({toks} tokens, all {case.h_v} value "
+                       f"heads), fp64 token loop, {t:.2f} s on {threads} threads; one "
+                       f"sequence ({first.total_tokens} tokens) on 1 thread in {t_one:.2f} s"}
+    return entry, seqs, S, o
+
+
+def parity_vs_oracle(S_gpu, o_gpu, case, seqs, S_ref, o_ref):
+    """Relative Frobenius error of the benchmarked launch's states and outputs
+    against the oracle on the sequences it ran, and the worst (sequence, head)
+    block of each."""
+    import numpy as np
+    import torch
+    cu = case.cu_seqlens
+    S = S_gpu[seqs].double().cpu().numpy()
+    rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+    o = o_gpu[torch.from_numpy(rows).to(o_gpu.device)].float().cpu().numpy()
+
+    def rel(x, r):
+        return float(np.linalg.norm(x - r) / np.linalg.norm(r))
+    worst_S = max(rel(S[i, h], S_ref[i, h]) for i in range(len(seqs)) for h in range(case.h_v))
+    worst_o, off = 0.0, 0
+    for s in seqs:
+        L = int(cu[s + 1] - cu[s])
+        for h in range(case.h_v):
+            worst_o = max(worst_o, rel(o[off:off + L, h], o_ref[off:off + L, h]))
+        off += L
+    return {"rel_S": rel(S, S_ref), "rel_o": rel(o, o_ref), "worst_head_S": worst_S,
+            "worst_head_o": worst_o, "sequences": f"{len(seqs)} of {case.n_seqs}",
+            "tolerance": 2e-3}
 
 
 def group_flops(T, hidden, h_k, h_v, d, n_gdn, chunk=64):
@@ -126,43 +168,36 @@ def group_flops(T, hidden, h_k, h_v, d, n_gdn, chunk=64):
     return f
 
 
-def timed(fn, steps, warmup):
+def time_steps(fn, steps, warmup):
+    """Time `steps` calls of fn after `warmup` untimed ones.  The timed region
+    is bracketed by device synchronisations; a HIP event on the current
+    stream (the stream the library launches on) follows every call, so both
+    the whole-run mean and the per-call distribution are measured.  Returns
+    milliseconds: mean (total / steps), median, p10, p90, min, max."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+
+    def pct(q):
+        return per[min(len(per) - 1, int(round(q * (len(per) - 1))))]
+    return {"mean_ms": ev[0].elapsed_time(ev[-1]) / steps, "median_ms": pct(0.5),
+            "p10_ms": pct(0.1), "p90_ms": pct(0.9), "min_ms": per[0], "max_ms": per[-1]}
 
 
-def time_launches(fn, steps, warmup):
-    """Average milliseconds per call of fn over `steps` calls, HIP events on
-    the current stream (the stream the library launches on)."""
-    import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(steps):
-        fn()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps
-
-
-def replay_entry(ms, T, byts, flops):
+def replay_entry(t, T, byts, flops):
+    ms = t["mean_ms"]
     sec = ms / 1e3
-    return {"ms_per_step": ms, "replayed_tokens_per_s": T / sec,
+    return {"ms_per_step": ms, "median_ms": t["median_ms"], "p10_ms": t["p10_ms"],
+            "p90_ms": t["p90_ms"], "replayed_tokens_per_s": T / sec,
             "hbm_gbs": byts / sec / 1e9, "hbm_frac": byts / sec / 1e9 / HBM_PEAK_GBS,
             "mfma_tflops": flops / sec / 1e12,
             "mfma_frac": flops / sec / 1e12 / MFMA_F16_PEAK_TFS,
@@ -179,31 +214,33 @@ def bench_replay_variants(steps, warmup, to_dev, q, k, v, alpha, beta, cu, S):
 
     n, L, hk, hv, d = S.shape[0], 3276, k.shape[1], v.shape[1], k.shape[2]
     T = k.shape[0]
-    ms = time_launches(lambda: sr.gdn_replay_state(None, k, v, alpha, beta, cu, None,
-                                                   alpha_is_log=True, want_o=False,
-                                                   final_state=S), steps, warmup)
+    t = time_steps(lambda: sr.gdn_replay_state(None, k, v, alpha, beta, cu, None,
+                                               alpha_is_log=True, want_o=False,
+                                               final_state=S), steps, warmup)
     byts, flops = gdn_algorithmic(n, L, hk, hv, d, want_o=False)
     out = {"state_only": dict(workload="headline replay without q and o (state only)",
-                              **replay_entry(ms, T, byts, flops))}
+                              **replay_entry(t, T, byts, flops))}
     c = config_c2()
     q2, k2, v2, a2, cu2 = (to_dev(x) for x in (c.q, c.k, c.v, c.alpha, c.cu_seqlens))
     S2 = torch.empty((c.n_seqs, c.h_v, c.d_k, c.d_v), dtype=torch.float32, device=k.device)
     o2 = torch.empty((c.total_tokens, c.h_v, c.d_v), dtype=torch.bfloat16, device=k.device)
-    ms = time_launches(lambda: sr.gdn_replay_state(q2, k2, v2, a2, None, cu2, None, erase=False,
-                                                   alpha_is_log=c.alpha_is_log,
-                                                   final_state=S2, o=o2), steps, warmup)
+    t = time_steps(lambda: sr.gdn_replay_state(q2, k2, v2, a2, None, cu2, None, erase=False,
+                                               alpha_is_log=c.alpha_is_log,
+                                               final_state=S2, o=o2), steps, warmup)
     byts, flops = gdn_algorithmic(c.n_seqs, c.total_tokens // c.n_seqs, c.h_k, c.h_v, c.d_k,
                                   erase=False)
     out["erase_free"] = dict(workload="erase-free (scalar decay) replay, 8 x 2048, 32 heads, "
                                       "d=128, bf16 in/out, beta = 1",
-                             **replay_entry(ms, c.total_tokens, byts, flops))
+                             **replay_entry(t, c.total_tokens, byts, flops))
     return out
 
 
 def bench_group(steps, warmup, to_dev):
-    """3-layer replay group (hidden 2560) from 4 x 1638 anchors, and the
-    varlen path: 64 hits gathered from a paged pool of full prefixes and
-    replayed through the same group shapes."""
+    """3-layer replay group (hidden 2560) from 4 x 1638 anchors; the varlen
+    path: 64 hits gathered from a paged pool of full prefixes and replayed
+    through the same group shapes; and the sparse-anchor path: the same 64
+    hits with anchors kept at density 1/16 next to each page boundary and a
+    replay of k = min(ceil(0.05 n), 512) anchors."""
     import numpy as np
     import torch
     import linear_attention_state_anchor_amd as sr
@@ -216,22 +253,18 @@ def bench_group(steps, warmup, to_dev):
     anchors, cu = to_dev(g.anchors), to_dev(g.cu_seqlens)
     T = g.total_tokens
     states = torch.empty((3, g.n_seqs, 32, 128, 128), dtype=torch.float32, device="cuda:0")
-    ws = torch.empty((1 << 20,), dtype=torch.uint8, device="cuda:0")
-    sr.replay_group(anchors, packed, cu, g.layer_kind, 16, 32, 128, states=states)
-    import ctypes
-    from linear_attention_state_anchor_amd import _lib
-    kinds = (ctypes.c_int32 * 4)(*g.layer_kind)
-    desc = _lib.GroupDesc(4, ctypes.cast(kinds, ctypes.POINTER(ctypes.c_int32)), 2560, 16, 32,
-                          128, 4, 1e-6, 1e-6, g.n_seqs, T, T)
-    wsb = int(_lib.load().sr_replay_group_workspace_bytes(ctypes.byref(desc)))
-    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda:0")
-    ms = timed(lambda: sr.replay_group(anchors, packed, cu, g.layer_kind, 16, 32, 128,
-                                       states=states, workspace=ws), steps, warmup)
+    ws = torch.empty((sr.group_workspace_bytes(T, 2560, 16, 32, 128, n_seqs=g.n_seqs,
+                                               layer_kind=g.layer_kind),),
+                     dtype=torch.uint8, device="cuda:0")
+    t = time_steps(lambda: sr.replay_group(anchors, packed, cu, g.layer_kind, 16, 32, 128,
+                                           states=states, workspace=ws), steps, warmup)
     fl = group_flops(T, 2560, 16, 32, 128, 3)
+    ms = t["mean_ms"]
     out["group"] = {
         "workload": "3 GDN layers + skipped FA, hidden 2560, 4 requests x 1638 anchors "
                     "(5% of 32K), bf16 anchors and weights",
-        "ms_per_step": ms, "replayed_tokens_per_s_per_layer": 3 * T / (ms / 1e3),
+        "ms_per_step": ms, "median_ms": t["median_ms"], "p10_ms": t["p10_ms"],
+        "p90_ms": t["p90_ms"], "replayed_tokens_per_s_per_layer": 3 * T / (ms / 1e3),
         "tflops": fl / (ms / 1e3) / 1e12, "mfma_frac": fl / (ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFS,
     }
     del ws
@@ -246,27 +279,63 @@ def bench_group(steps, warmup, to_dev):
     T5 = int(pc.suffix_len.sum())
     packed_anchors = torch.empty((T5, 2560), dtype=torch.bfloat16, device="cuda:0")
     cu5 = torch.empty((65,), dtype=torch.int32, device="cuda:0")
-    desc5 = _lib.GroupDesc(4, ctypes.cast(kinds, ctypes.POINTER(ctypes.c_int32)), 2560, 16, 32,
-                           128, 4, 1e-6, 1e-6, 64, T5, int(pc.suffix_len.max()))
-    ws5 = torch.empty((int(_lib.load().sr_replay_group_workspace_bytes(ctypes.byref(desc5))),),
+    ws5 = torch.empty((sr.group_workspace_bytes(T5, 2560, 16, 32, 128, n_seqs=64),),
                       dtype=torch.uint8, device="cuda:0")
     states5 = torch.empty((3, 64, 32, 128, 128), dtype=torch.float32, device="cuda:0")
     gather = lambda: sr.gather_suffix(pool, pt, ml, sl, T5, packed=packed_anchors, cu_seqlens=cu5)
-    ms_g = timed(gather, steps, warmup)
+    tg = time_steps(gather, steps, warmup)
+
     def path():
         gather()
         sr.replay_group(packed_anchors, packed5, cu5, [0, 0, 0, 1], 16, 32, 128,
-                        states=states5, workspace=ws5)
-    ms_p = timed(path, max(2, steps // 5), 1)
+                        max_seqlen=int(pc.suffix_len.max()), states=states5, workspace=ws5)
+    tp = time_steps(path, max(2, steps // 5), 1)
     fl5 = group_flops(T5, 2560, 16, 32, 128, 3)
     gb = 2 * T5 * 2560 * 2 / 1e9
+    ms_p, ms_g = tp["mean_ms"], tg["mean_ms"]
     out["varlen"] = {
         "workload": f"64 hits, m ~ U{{8192..32768}}, k = ceil(r m), r ~ U[0.05,0.10] "
                     f"(T = {T5}), gather from 64-token pages + 3-layer group, hidden 2560",
-        "ms_per_step": ms_p, "replayed_tokens_per_s_per_layer": 3 * T5 / (ms_p / 1e3),
-        "tflops": fl5 / (ms_p / 1e3) / 1e12,
-        "gather_ms": ms_g, "gather_gbs": gb / (ms_g / 1e3),
+        "ms_per_step": ms_p, "median_ms": tp["median_ms"],
+        "replayed_tokens_per_s_per_layer": 3 * T5 / (ms_p / 1e3),
+        "tflops": fl5 / (ms_p / 1e3) / 1e12, "mfma_frac": fl5 / (ms_p / 1e3) / 1e12 / MFMA_F16_PEAK_TFS,
+        "gather_ms": ms_g, "gather_median_ms": tg["median_ms"], "gather_gbs": gb / (ms_g / 1e3),
         "gather_hbm_frac": gb / (ms_g / 1e3) / HBM_PEAK_GBS,
+    }
+    del pool, ws5, packed_anchors
+    # sparse anchors: 4 of every 64 positions (next to the page boundary)
+    offs = sr.DENSE_NEAR_BOUNDARY_1_16
+    m = [int(x) for x in pc.matched_len]
+    n_anchor = [len(offs) * (x // PAGE) + sum(o < x % PAGE for o in offs) for x in m]
+    k_sp = sr.replay_budget(n_anchor, 0.05, 512)
+    Ts = sum(k_sp)
+    spool = torch.randn((pc.n_pages, len(offs), 2560), generator=gen, device="cuda:0",
+                        dtype=torch.float32).to(torch.bfloat16)
+    ksp = to_dev(np.asarray(k_sp, np.int32))
+    sp_anchors = torch.empty((Ts, 2560), dtype=torch.bfloat16, device="cuda:0")
+    cus = torch.empty((65,), dtype=torch.int32, device="cuda:0")
+    wss = torch.empty((sr.group_workspace_bytes(Ts, 2560, 16, 32, 128, n_seqs=64),),
+                      dtype=torch.uint8, device="cuda:0")
+    sgather = lambda: sr.gather_anchors(spool, offs, pt, ml, ksp, Ts, packed=sp_anchors,
+                                        cu_seqlens=cus, positions=False)
+    tsg = time_steps(sgather, steps, warmup)
+
+    def spath():
+        sgather()
+        sr.replay_group(sp_anchors, packed5, cus, [0, 0, 0, 1], 16, 32, 128,
+                        max_seqlen=max(k_sp), states=states5, workspace=wss)
+    tsp = time_steps(spath, steps, warmup)
+    fls = group_flops(Ts, 2560, 16, 32, 128, 3)
+    ms_s = tsp["mean_ms"]
+    out["sparse_anchors"] = {
+        "workload": f"the same 64 hits with anchors at density 1/16 next to each page "
+                    f"boundary, k = min(ceil(0.05 n), 512) anchors (T = {Ts}), gather + "
+                    f"3-layer group, hidden 2560",
+        "ms_per_step": ms_s, "median_ms": tsp["median_ms"],
+        "replayed_anchors_per_s_per_layer": 3 * Ts / (ms_s / 1e3),
+        "tflops": fls / (ms_s / 1e3) / 1e12,
+        "gather_ms": tsg["mean_ms"],
+        "gather_gbs": 2 * Ts * 2560 * 2 / 1e9 / (tsg["mean_ms"] / 1e3),
     }
     return out
 
@@ -363,18 +432,8 @@ def main():
         sr.gdn_replay_state(q, k, v, alpha, beta, cu, None, alpha_is_log=True,
                             final_state=S, o=o)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    t = time_steps(step, args.steps, args.warmup)
+    ms = t["mean_ms"]
     assert bool(torch.isfinite(S).all()), "non-finite state"
 
     byts, flops = gdn_algorithmic(n, L, hk, hv, d)
@@ -390,6 +449,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "median_ms": t["median_ms"], "p10_ms": t["p10_ms"], "p90_ms": t["p90_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -416,6 +476,7 @@ def main():
             "frac": flops / sec / 1e12 / MFMA_F16_PEAK_TFS,
             "flop_per_launch": flops,
             "bytes_per_launch": byts,
+            "flop_count": "chunked algorithm with the C x C tile products counted dense",
         },
     }
     line.update(bench_replay_variants(min(50, args.steps), 10, to_dev, q, k, v, alpha, beta,
@@ -423,7 +484,12 @@ def main():
     if not args.no_group:
         line.update(bench_group(min(20, max(3, args.steps // 5)), 3, to_dev))
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        # the benchmarked launch's S and o, against the oracle
+        step()
+        torch.cuda.synchronize()
+        entry, seqs, S_ref, o_ref = cpu_baseline(case, args.cpu_budget)
+        line["cpu_baseline"] = entry
+        line["parity"] = parity_vs_oracle(S, o, case, seqs, S_ref, o_ref)
     if args.copy_calib:
         src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

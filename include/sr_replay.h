@@ -17,10 +17,15 @@
  *  - Arguments are checked on the host first.  On any failure nothing is
  *    enqueued and a nonzero SR_E* code is returned (sr_status_str() names
  *    it).  A failed kernel launch returns SR_ELAUNCH.
- *  - Preconditions that live in device memory are documented, not checked:
- *    cu_seqlens non-decreasing with cu[0] = 0 and cu[N] = total_tokens;
- *    alpha in (0, 1] (log alpha in [-inf, 0]; values below -64 are clamped);
- *    page ids in range.
+ *  - Preconditions that live in device memory are documented, and checked
+ *    only on request: cu_seqlens non-decreasing with cu[0] = 0 and
+ *    cu[N] = total_tokens; alpha in (0, 1] (log alpha in [-inf, 0]; values
+ *    below -64 are clamped); beta in [0, 2]; replay lengths 0 <= k_i <= m_i
+ *    and page ids in range.  sr_check_replay_inputs / sr_check_gather_inputs
+ *    run a validation kernel over them and return SR_EDATA on a violation
+ *    (they synchronise the stream).  With the environment variable SR_DEBUG
+ *    set to 1, every entry point runs the matching check first and returns
+ *    its status before anything else is enqueued.
  *  - Packed varlen tensors are token-major: row t of a [T][...] tensor holds
  *    token t of the concatenation of all sequences, as cu_seqlens splits it.
  *  - Results are deterministic (no atomics in reductions): repeated calls on
@@ -46,6 +51,8 @@ extern "C" {
 #define SR_EWORKSPACE 4 /* workspace missing or too small                   */
 #define SR_ELAUNCH 5    /* a kernel launch failed (HIP error)               */
 #define SR_EDEVICE 6    /* no usable gfx950 device                          */
+#define SR_EDATA 7      /* device-side inputs break a documented precondition
+                           (only reported by the validation checks)         */
 
 /* element types */
 #define SR_BF16 0
@@ -94,7 +101,17 @@ const char* sr_status_str(int status);
  * on load, which is exact for |x| in [2^-14, 65504]; larger magnitudes are
  * outside the contract.  dtype_o: SR_BF16, SR_F16 or SR_F32.
  * n_seqs = 0 or total_tokens = 0 is allowed; an empty sequence returns its
- * initial state.  No workspace.
+ * initial state.
+ *
+ * State magnitude: the chunked kernel keeps each wave's part of the state as
+ * 2^E times a register copy (E >= 0 chosen per chunk), so the fp16 operand
+ * copies of the state stay in range for states of any fp32 magnitude.
+ *
+ * Workspace: sr_gdn_workspace_bytes() bytes (currently 0 for every
+ * supported shape; workspace may then be NULL).  Status: SR_EINVAL for a
+ * null required pointer, a bad flag or a misaligned q/k/v/o (16-byte rows,
+ * 8-byte outputs); SR_ESHAPE for unsupported sizes; SR_EDTYPE;
+ * SR_EWORKSPACE; SR_ELAUNCH.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t n_seqs;       /* N >= 0                                          */
@@ -120,8 +137,18 @@ typedef struct {
   void* o;
 } sr_gdn_io;
 
+/* Workspace bytes sr_gdn_replay_state needs for this descriptor (0 when it
+ * needs none; (size_t)-1 for a descriptor it rejects). */
+size_t sr_gdn_workspace_bytes(const sr_gdn_desc* desc);
+
 int sr_gdn_replay_state(const sr_gdn_desc* desc, const sr_gdn_io* io,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Validation of the device-side preconditions of one sr_gdn_replay_state
+ * call (cu_seqlens, alpha, beta as described above).  Runs a kernel on
+ * `stream`, waits for it and returns SR_OK, SR_EDATA, or the host-side
+ * argument status of sr_gdn_replay_state. */
+int sr_check_replay_inputs(const sr_gdn_desc* desc, const sr_gdn_io* io, void* stream);
 
 /* --------------------------------------------------------------------------
  * Anchor gather and varlen packing ("SuffixReplay", Algorithm Design 2:
@@ -142,7 +169,9 @@ int sr_gdn_replay_state(const sr_gdn_desc* desc, const sr_gdn_io* io,
  *               untouched)
  *   cu_seqlens_out [n_req+1] int32
  * hidden * elem_bytes must be a multiple of 16.  The host-side total keeps
- * the launch free of a device-to-host read.
+ * the launch free of a device-to-host read.  Out-of-range page ids and
+ * page-table columns are clamped (the launch stays in bounds; the copied
+ * rows are then meaningless): sr_check_gather_inputs reports them.
  * ------------------------------------------------------------------------ */
 int sr_gather_suffix(const void* pool, int32_t hidden, int32_t elem_bytes,
                      int64_t n_pages, const int32_t* page_table,
@@ -150,6 +179,61 @@ int sr_gather_suffix(const void* pool, int32_t hidden, int32_t elem_bytes,
                      const int32_t* suffix_len, int32_t n_req,
                      int32_t total_tokens, void* packed,
                      int32_t* cu_seqlens_out, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Gather with token-wise sparse anchors ("SuffixReplay", Algorithm Design 2,
+ * Figure 3: anchors kept at a subset of positions aligned with the 64-token
+ * pages, e.g. density 1/16; sampled densely next to the page boundary; and
+ * Algorithm Design 3: the replay length counts anchors).
+ *
+ * Every 64-token page p of a prefix owns one anchor block of A rows (the
+ * block sits in the same page slot, so the KV page table indexes it); row j
+ * of the block holds the anchor at position 64 p + page_offsets[j].  A = 64
+ * with offsets 0..63 is the dense case (sr_gather_suffix); density 1/16
+ * sampled next to the boundary is A = 4 with offsets 60, 61, 62, 63.
+ *
+ * Request i's anchors are the positions 64 p + page_offsets[j] < m_i in
+ * increasing order, n_i = A floor(m_i / 64) + #{j : page_offsets[j] <
+ * m_i mod 64} of them; the packed rows cu[i] .. cu[i]+k_i-1 receive its
+ * last k_i anchors (0 <= k_i <= n_i), and positions_out (may be NULL) the
+ * prefix position of each packed row.
+ *
+ *   pool          [n_blocks][A][hidden], elem_bytes per element (bitwise)
+ *   page_offsets  HOST [A], strictly increasing, in [0, 64); 1 <= A <= 64
+ *   page_table, matched_len (tokens), suffix_len (anchors), cu_seqlens_out
+ *                 as for sr_gather_suffix
+ *   positions_out [total_tokens] int32 or NULL
+ * ------------------------------------------------------------------------ */
+int sr_gather_anchors(const void* pool, int32_t hidden, int32_t elem_bytes,
+                      int64_t n_blocks, int32_t anchors_per_page,
+                      const int32_t* page_offsets, const int32_t* page_table,
+                      int32_t pt_stride, const int32_t* matched_len,
+                      const int32_t* suffix_len, int32_t n_req,
+                      int32_t total_tokens, void* packed,
+                      int32_t* cu_seqlens_out, int32_t* positions_out,
+                      void* stream);
+
+/* Validation of a gather's device-side preconditions: m_i >= 0,
+ * 0 <= k_i <= n_i (the anchors of request i; n_i = m_i for dense
+ * anchors), every page-table column a replay reads below pt_stride and its
+ * page id in [0, n_blocks), and sum k_i = total_tokens.  anchors_per_page /
+ * page_offsets as for sr_gather_anchors (64 and NULL for dense anchors).
+ * Runs a kernel, waits for it, returns SR_OK, SR_EDATA or a host-side
+ * argument status. */
+int sr_check_gather_inputs(int64_t n_blocks, int32_t anchors_per_page,
+                           const int32_t* page_offsets, const int32_t* page_table,
+                           int32_t pt_stride, const int32_t* matched_len,
+                           const int32_t* suffix_len, int32_t n_req,
+                           int32_t total_tokens, void* stream);
+
+/* Replay budget ("SuffixReplay", Algorithm Design 3: the replay length, in
+ * anchors, is min(0.05 n, k_max); "Tail-Replay", section 3: a fixed share
+ * of the matched prefix).  k[i] = min(ceil(ratio * n_anchors[i]), k_max),
+ * n_anchors[i] the anchors of request i's matched prefix; k_max <= 0 means
+ * no cap.  Host function (host arrays); returns sum k[i], or -1 for bad
+ * arguments (ratio outside (0, 1], a negative count, n_req < 0). */
+int64_t sr_replay_budget(const int32_t* n_anchors, int32_t n_req, double ratio,
+                         int32_t k_max, int32_t* k);
 
 /* --------------------------------------------------------------------------
  * Replay of one group of linear-attention layers from its entry anchors
@@ -170,8 +254,11 @@ int sr_gather_suffix(const void* pool, int32_t hidden, int32_t elem_bytes,
  *   RMSNorm per value head, unit weight, rms_eps), W_out [h_v d][hidden]
  *   the last GDN layer only produces its state.
  *
- * Weights come pre-packed (sr_pack_gdn_layer) because the matrix-core
- * kernels read them k-contiguous in fp16.
+ * Weights come pre-packed (sr_pack_gdn_layer): the matrix-core kernels read
+ * them k-contiguous in fp16, and a layer's weights are static, so the
+ * re-layout is done once when the weights are loaded rather than on every
+ * replay.  The raw bf16 {w_in, conv_w, w_out} triple is what
+ * sr_pack_gdn_layer takes.
  *
  *   anchors     [T][hidden] bf16
  *   cu_seqlens  [n_seqs+1] int32 (device)
@@ -184,7 +271,7 @@ int sr_gather_suffix(const void* pool, int32_t hidden, int32_t elem_bytes,
  *   workspace   >= sr_replay_group_workspace_bytes(desc) bytes, 256-aligned
  *
  * Supported: h_v % h_k == 0, d in {64, 128}, conv_width in 2..8,
- * hidden % 64 == 0.  FA layers may lead or trail the GDN layers but not sit
+ * hidden % 128 == 0.  FA layers may lead or trail the GDN layers but not sit
  * between them (one anchor tensor feeds one contiguous run of GDN layers).
  * ------------------------------------------------------------------------ */
 typedef struct {

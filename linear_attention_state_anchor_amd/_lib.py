@@ -12,7 +12,10 @@ import threading
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsr_replay.so")
 
-SR_OK, SR_EINVAL, SR_ESHAPE, SR_EDTYPE, SR_EWORKSPACE, SR_ELAUNCH, SR_EDEVICE = range(7)
+SR_OK, SR_EINVAL, SR_ESHAPE, SR_EDTYPE, SR_EWORKSPACE, SR_ELAUNCH, SR_EDEVICE, SR_EDATA = range(8)
+# statuses that mean "the arguments (or the device data they point to) are
+# outside the contract", raised as ValueError
+ARGUMENT_STATUSES = (SR_EINVAL, SR_ESHAPE, SR_EDTYPE, SR_EWORKSPACE, SR_EDATA)
 SR_BF16, SR_F16, SR_F32 = 0, 1, 2
 SR_LAYER_GDN, SR_LAYER_FA = 0, 1
 
@@ -49,9 +52,20 @@ class LayerWeights(ctypes.Structure):
 SIGNATURES = {
     "sr_version": (ctypes.c_char_p, []),
     "sr_status_str": (ctypes.c_char_p, [ctypes.c_int]),
-    "sr_gdn_replay_state": (ctypes.c_int, [ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnIO), c_p]),
+    "sr_gdn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(GdnDesc)]),
+    "sr_gdn_replay_state": (ctypes.c_int, [ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnIO), c_p,
+                                           ctypes.c_size_t, c_p]),
+    "sr_check_replay_inputs": (ctypes.c_int, [ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnIO),
+                                              c_p]),
     "sr_gather_suffix": (ctypes.c_int, [c_p, c_i32, c_i32, ctypes.c_int64, c_p, c_i32, c_p,
                                         c_p, c_i32, c_i32, c_p, c_p, c_p]),
+    "sr_gather_anchors": (ctypes.c_int, [c_p, c_i32, c_i32, ctypes.c_int64, c_i32,
+                                         ctypes.POINTER(c_i32), c_p, c_i32, c_p, c_p, c_i32,
+                                         c_i32, c_p, c_p, c_p, c_p]),
+    "sr_check_gather_inputs": (ctypes.c_int, [ctypes.c_int64, c_i32, ctypes.POINTER(c_i32), c_p,
+                                              c_i32, c_p, c_p, c_i32, c_i32, c_p]),
+    "sr_replay_budget": (ctypes.c_int64, [ctypes.POINTER(c_i32), c_i32, ctypes.c_double, c_i32,
+                                          ctypes.POINTER(c_i32)]),
     "sr_packed_layer_bytes": (ctypes.c_size_t, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "sr_pack_gdn_layer": (ctypes.c_int, [c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                          c_p, c_p]),
@@ -65,12 +79,17 @@ _lock = threading.Lock()
 
 
 class ReplayError(RuntimeError):
-    """A nonzero status from the C ABI."""
+    """A nonzero status from the C ABI (launch or device failures)."""
 
     def __init__(self, fn, status):
         self.status = status
         msg = load().sr_status_str(status).decode()
         super().__init__(f"{fn} failed: status {status} ({msg})")
+
+
+class ReplayArgumentError(ReplayError, ValueError):
+    """A status that rejects the arguments (or the device data they point to):
+    SR_EINVAL, SR_ESHAPE, SR_EDTYPE, SR_EWORKSPACE, SR_EDATA."""
 
 
 def load():
@@ -94,4 +113,6 @@ def load():
 
 def check(fn, status):
     if status != SR_OK:
+        if status in ARGUMENT_STATUSES:
+            raise ReplayArgumentError(fn, status)
         raise ReplayError(fn, status)

@@ -1,16 +1,24 @@
 // Anchor gather and varlen packing ("SuffixReplay", Algorithm Design 2:
-// anchors live on 64-token pages; System Design, Pipelined Replay Path:
-// several hits are packed into one variable-length batch with device-side
-// boundaries).
+// anchors on 64-token pages, optionally kept at only a subset of positions;
+// Algorithm Design 3: the replay length counts anchors; System Design,
+// Pipelined Replay Path: several hits are packed into one variable-length
+// batch with device-side boundaries).
+//
+// Every 64-token page p of a prefix owns an anchor block of A rows; row j
+// holds the anchor at position 64 p + off[j] (A = 64, off = 0..63: every
+// token is an anchor).  Request i with matched length m_i has
+// n_i = A floor(m_i / 64) + #{j : off[j] < m_i mod 64} anchors, in position
+// order; its replay is the last k_i of them.
 //
 // Kernel 1 (one workgroup) writes cu = exclusive prefix sum of the replay
 // lengths.  Kernel 2 copies one packed row per wave with 16-byte vector
 // loads/stores: packed row r belongs to the request i with cu[i] <= r <
-// cu[i+1] (binary search), prefix position p = m_i - k_i + (r - cu[i]),
-// source page page_table[i][p / 64], row p % 64.  Page ids and page-table
-// columns are clamped into range so a corrupt table cannot read outside the
-// pool (the copied data is then meaningless, but the launch stays in bounds).
+// cu[i+1] (binary search), anchor a = n_i - k_i + (r - cu[i]), source block
+// page_table[i][a / A], row a % A.  Page ids and page-table columns are
+// clamped into range so a corrupt table cannot read outside the pool (the
+// copied data is then meaningless, but the launch stays in bounds).
 #include <stdint.h>
+#include <math.h>
 
 #include "sr_common.hpp"
 #include "sr_internal.hpp"
@@ -19,6 +27,20 @@ namespace sr {
 namespace {
 
 constexpr int kPage = 64;
+
+struct AnchorLayout {
+  int a;        // anchor rows per page (1..64)
+  int dense;    // 1: a = 64 and off[j] = j
+  int off[64];  // in-page positions, strictly increasing
+};
+
+__device__ __forceinline__ int64_t anchors_in(int64_t m, const AnchorLayout& L) {
+  if (L.dense) return m;
+  int64_t n = (m / kPage) * L.a;
+  const int rem = static_cast<int>(m % kPage);
+  for (int j = 0; j < L.a; ++j) n += L.off[j] < rem;
+  return n;
+}
 
 __global__ __launch_bounds__(1024) void suffix_cu_kernel(const int32_t* __restrict__ k,
                                                           int n, int32_t* __restrict__ cu) {
@@ -53,10 +75,10 @@ __global__ __launch_bounds__(1024) void suffix_cu_kernel(const int32_t* __restri
 }
 
 __global__ __launch_bounds__(256) void gather_rows_kernel(
-    const uint8_t* __restrict__ pool, int64_t n_pages, int row_bytes,
+    const uint8_t* __restrict__ pool, int64_t n_blocks, int row_bytes, AnchorLayout lay,
     const int32_t* __restrict__ pt, int pt_stride, const int32_t* __restrict__ m_len,
     const int32_t* __restrict__ k_len, int n_req, const int32_t* __restrict__ cu,
-    int total, uint8_t* __restrict__ out) {
+    int total, uint8_t* __restrict__ out, int32_t* __restrict__ positions) {
   const int r = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (r >= total || r >= cu[n_req]) return;  // rows past sum(k) stay untouched
@@ -68,17 +90,68 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(
     else hi = mid - 1;
   }
   const int i = lo;
-  int p = m_len[i] - k_len[i] + (r - cu[i]);
-  p = max(p, 0);
-  const int col = min(p / kPage, pt_stride - 1);
+  int64_t a = anchors_in(m_len[i], lay) - k_len[i] + (r - cu[i]);
+  a = a < 0 ? 0 : a;
+  const int64_t pcol = a / lay.a;
+  const int j = static_cast<int>(a % lay.a);
+  const int col = static_cast<int>(pcol < pt_stride - 1 ? pcol : pt_stride - 1);
   int64_t page = pt[static_cast<int64_t>(i) * pt_stride + col];
-  page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
-  const uint8_t* src = pool + (page * kPage + (p % kPage)) * static_cast<int64_t>(row_bytes);
+  page = page < 0 ? 0 : (page >= n_blocks ? n_blocks - 1 : page);
+  const uint8_t* src = pool + (page * lay.a + j) * static_cast<int64_t>(row_bytes);
   uint8_t* dst = out + static_cast<int64_t>(r) * row_bytes;
   const int nvec = row_bytes / 16;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   for (int e = lane; e < nvec; e += kWave)
     reinterpret_cast<u32x4*>(dst)[e] = reinterpret_cast<const u32x4*>(src)[e];
+  if (positions && lane == 0)
+    positions[r] = static_cast<int32_t>(pcol * kPage + (lay.dense ? j : lay.off[j]));
+}
+
+int gather(const void* pool, int32_t hidden, int32_t elem_bytes, int64_t n_blocks,
+           int32_t anchors_per_page, const int32_t* page_offsets, const int32_t* page_table,
+           int32_t pt_stride, const int32_t* matched_len, const int32_t* suffix_len,
+           int32_t n_req, int32_t total_tokens, void* packed, int32_t* cu_seqlens_out,
+           int32_t* positions_out, void* stream) {
+  if (n_req < 0 || total_tokens < 0 || hidden < 1 || pt_stride < 1) return SR_ESHAPE;
+  if (elem_bytes != 2 && elem_bytes != 4) return SR_EDTYPE;
+  if (anchors_per_page < 1 || anchors_per_page > kPage) return SR_ESHAPE;
+  AnchorLayout lay{};
+  lay.a = anchors_per_page;
+  lay.dense = page_offsets == nullptr && anchors_per_page == kPage;
+  if (!page_offsets && !lay.dense) return SR_EINVAL;
+  for (int j = 0; j < lay.a; ++j) {
+    lay.off[j] = page_offsets ? page_offsets[j] : j;
+    if (lay.off[j] < 0 || lay.off[j] >= kPage || (j > 0 && lay.off[j] <= lay.off[j - 1]))
+      return SR_ESHAPE;
+  }
+  if (lay.a == kPage) lay.dense = 1;  // offsets 0..63 are the only increasing choice
+  const int64_t row_bytes = static_cast<int64_t>(hidden) * elem_bytes;
+  if (row_bytes % 16 != 0 || row_bytes > INT32_MAX) return SR_ESHAPE;
+  if (!cu_seqlens_out) return SR_EINVAL;
+  if (n_req > 0 && (!matched_len || !suffix_len)) return SR_EINVAL;
+  if (total_tokens > 0 && (n_req == 0 || !pool || !page_table || !packed || n_blocks < 1))
+    return n_req == 0 ? SR_ESHAPE : SR_EINVAL;
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (total_tokens > 0 && (!al16(pool) || !al16(packed))) return SR_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_checks_enabled()) {
+    const int c = check_gather(n_blocks, lay.a, lay.off, page_table, pt_stride, matched_len,
+                               suffix_len, n_req, total_tokens, s);
+    if (c != SR_OK) return c;
+  }
+  hipLaunchKernelGGL(suffix_cu_kernel, dim3(1), dim3(1024), 0, s, suffix_len, n_req,
+                     cu_seqlens_out);
+  if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+  if (total_tokens > 0) {
+    const int blocks = (total_tokens + 3) / 4;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(pool), n_blocks, static_cast<int>(row_bytes),
+                       lay, page_table, pt_stride, matched_len, suffix_len, n_req,
+                       cu_seqlens_out, total_tokens, static_cast<uint8_t*>(packed),
+                       positions_out);
+    if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+  }
+  return SR_OK;
 }
 
 }  // namespace
@@ -90,27 +163,43 @@ extern "C" int sr_gather_suffix(const void* pool, int32_t hidden, int32_t elem_b
                                 const int32_t* suffix_len, int32_t n_req,
                                 int32_t total_tokens, void* packed,
                                 int32_t* cu_seqlens_out, void* stream) {
-  if (n_req < 0 || total_tokens < 0 || hidden < 1 || pt_stride < 1) return SR_ESHAPE;
-  if (elem_bytes != 2 && elem_bytes != 4) return SR_EDTYPE;
-  const int64_t row_bytes = static_cast<int64_t>(hidden) * elem_bytes;
-  if (row_bytes % 16 != 0 || row_bytes > INT32_MAX) return SR_ESHAPE;
-  if (!cu_seqlens_out) return SR_EINVAL;
-  if (n_req > 0 && (!matched_len || !suffix_len)) return SR_EINVAL;
-  if (total_tokens > 0 && (n_req == 0 || !pool || !page_table || !packed || n_pages < 1))
-    return n_req == 0 ? SR_ESHAPE : SR_EINVAL;
-  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  if (total_tokens > 0 && (!al16(pool) || !al16(packed))) return SR_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(sr::suffix_cu_kernel, dim3(1), dim3(1024), 0, s, suffix_len, n_req,
-                     cu_seqlens_out);
-  if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
-  if (total_tokens > 0) {
-    const int blocks = (total_tokens + 3) / 4;
-    hipLaunchKernelGGL(sr::gather_rows_kernel, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(pool), n_pages, static_cast<int>(row_bytes),
-                       page_table, pt_stride, matched_len, suffix_len, n_req,
-                       cu_seqlens_out, total_tokens, static_cast<uint8_t*>(packed));
-    if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+  return sr::gather(pool, hidden, elem_bytes, n_pages, sr::kPage, nullptr, page_table, pt_stride,
+                    matched_len, suffix_len, n_req, total_tokens, packed, cu_seqlens_out,
+                    nullptr, stream);
+}
+
+extern "C" int sr_gather_anchors(const void* pool, int32_t hidden, int32_t elem_bytes,
+                                 int64_t n_blocks, int32_t anchors_per_page,
+                                 const int32_t* page_offsets, const int32_t* page_table,
+                                 int32_t pt_stride, const int32_t* matched_len,
+                                 const int32_t* suffix_len, int32_t n_req,
+                                 int32_t total_tokens, void* packed,
+                                 int32_t* cu_seqlens_out, int32_t* positions_out,
+                                 void* stream) {
+  if (!page_offsets) return SR_EINVAL;
+  return sr::gather(pool, hidden, elem_bytes, n_blocks, anchors_per_page, page_offsets,
+                    page_table, pt_stride, matched_len, suffix_len, n_req, total_tokens, packed,
+                    cu_seqlens_out, positions_out, stream);
+}
+
+extern "C" int64_t sr_replay_budget(const int32_t* n_anchors, int32_t n_req, double ratio,
+                                    int32_t k_max, int32_t* k) {
+  if (n_req < 0 || !(ratio > 0.0 && ratio <= 1.0)) return -1;
+  if (n_req > 0 && (!n_anchors || !k)) return -1;
+  int64_t sum = 0;
+  for (int32_t i = 0; i < n_req; ++i) {
+    const int32_t n = n_anchors[i];
+    if (n < 0) return -1;
+    // ceil(ratio * n) of the decimal ratio: a product within 1e-9 above an
+    // integer counts as that integer (0.05 or 0.07 are not exact in binary,
+    // and e.g. 0.07 * 100 evaluates to 7.000000000000001)
+    const double x = ratio * static_cast<double>(n);
+    const double fl = floor(x);
+    int64_t want = static_cast<int64_t>(x - fl <= 1e-9 ? fl : fl + 1.0);
+    if (want > n) want = n;
+    if (k_max > 0 && want > k_max) want = k_max;
+    k[i] = static_cast<int32_t>(want);
+    sum += want;
   }
-  return SR_OK;
+  return sum;
 }

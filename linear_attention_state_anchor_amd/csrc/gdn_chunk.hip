@@ -62,6 +62,16 @@ constexpr int kXcd = 8;        // XCDs; workgroups are dealt round-robin
 // s_waitcnt immediate for vmcnt(0) with the other counters unconstrained
 // (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
 constexpr int kWaitVmcnt0 = 0x0F70;
+// State exponent.  Each wave keeps its columns of the state as S = 2^E S_reg
+// (E >= 0, wave-uniform) and its U and outputs in the same units, so that
+// the fp16 copies of S_reg and U stay far inside fp16's range (65504) for a
+// state of any fp32 magnitude.  At every chunk start the wave checks
+// max |S_reg|: above kSHi, or below kSLo while E > 0, it rescales S_reg by a
+// power of two (exact) so the maximum lands just under 2^kSTarget.  States of
+// ordinary size keep E = 0, where the arithmetic is the unscaled one.
+constexpr float kSHi = 256.0f;
+constexpr float kSLo = 8.0f;
+constexpr int kSTarget = 7;
 
 template <int D, int HP>
 struct ChunkSmem {
@@ -519,6 +529,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
     prefetch_all(t_begin);
     prepare(t_begin);
   }
+  int sexp = 0;  // state exponent E of this wave (S = 2^E S_reg)
 
   for (int c0 = t_begin; c0 < t_end; c0 += kC) {
     const int nv = min(kC, t_end - c0);
@@ -589,6 +600,38 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
     }
     __syncthreads();
 
+    // ---- state exponent check (S = 2^E S_reg) -----------------------------
+    {
+      float m = 0.0f;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(S[jt][it][r]));
+      const bool over = __builtin_amdgcn_ballot_w64(m > kSHi) != 0;
+      const bool under = sexp > 0 && __builtin_amdgcn_ballot_w64(m >= kSLo) == 0;
+      if (over || under) {
+        // rare: rescale S_reg so that its maximum lands just under 2^kSTarget
+        const float mw = wave_max_nonneg(m);
+        int e = 0;
+        (void)frexpf(mw, &e);  // mw < 2^e
+        int k = (mw > 0.0f && mw <= 3.0e38f) ? e - kSTarget : -sexp;
+        k = max(k, -sexp);     // E stays >= 0
+        k = min(k, 100);
+        k = __builtin_amdgcn_readfirstlane(k);
+        sexp += k;
+        const float f = ldexpf(1.0f, -k);
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) S[jt][it] *= f;
+      }
+    }
+    // 2^-E: applied to V (so U is in the state's units); 2^E: to the outputs
+    const float s_dn = ldexpf(1.0f, -sexp);
+    const float s_up = ldexpf(1.0f, sexp);
+
     // U accumulators: tile (tt, it) = token rows 16tt.., value columns
     // w*IW + 16it..
     f32x4 U[4][NIT];
@@ -623,26 +666,33 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
         }
       }
     }
+    // erase: R~ = 2^-E V - e^G (K S_reg^T) (b is applied by the solve);
+    // erase-free: U = 2^-E diag(b) V.  The 2^-E factor is exact; the
+    // unscaled variant is the common one (E = 0).
+    auto rhs_v = [&](auto scaled) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      // erase: R~ = V - e^G (K S^T) (b is applied by the solve); erase-free:
-      // U = diag(b) V
-      const f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[hp][16 * tt + 4 * lg]);
-      const f32x4 ga4 = *reinterpret_cast<const f32x4*>(&sm.gam[hp][16 * tt + 4 * lg]);
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[hp][16 * tt + 4 * lg]);
+        const f32x4 ga4 = *reinterpret_cast<const f32x4*>(&sm.gam[hp][16 * tt + 4 * lg]);
+        if constexpr (decltype(scaled)::value && !ERASE) be4 *= s_dn;
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const u16x4 vx = lds_tr4(xv, 2 * (16 * tt * kWS + 16 * it));
+        for (int it = 0; it < NIT; ++it) {
+          const u16x4 vx = lds_tr4(xv, 2 * (16 * tt * kWS + 16 * it));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float vv = raw_to_f32<TI>(vx[r]);
-          U[tt][it][r] = ERASE ? fmaf(-ga4[r], U[tt][it][r], vv) : vv * be4[r];
+          for (int r = 0; r < 4; ++r) {
+            float vv = raw_to_f32<TI>(vx[r]);
+            if constexpr (decltype(scaled)::value && ERASE) vv *= s_dn;
+            U[tt][it][r] = ERASE ? fmaf(-ga4[r], U[tt][it][r], vv) : vv * be4[r];
+          }
+          // pinned in fp32: the solve rounds it to fp16, and a fused
+          // FMA-with-conversion in some template instances only would make
+          // the state-only and full replays differ in the last bit
+          asm volatile("" : "+v"(U[tt][it]));
         }
-        // pinned in fp32: the solve rounds it to fp16, and a fused
-        // FMA-with-conversion in some template instances only would make the
-        // state-only and full replays differ in the last bit
-        asm volatile("" : "+v"(U[tt][it]));
       }
-    }
+    };
+    if (sexp == 0) rhs_v(std::false_type{});
+    else rhs_v(std::true_type{});
     tr_keep(xv);
     if (ERASE) {
       // ---- block forward substitution (I + A) U = diag(b) R~, this wave's
@@ -741,6 +791,10 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
 #pragma unroll
             for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(U16[ks][it], pb, O[u][it]);
           }
+          if (sexp != 0) {  // back from the state's units (exact)
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) O[u][it] *= s_up;
+          }
           if (t < nv) {
             // uniform base (this chunk, this head) + 32-bit lane offset
             constexpr unsigned kOB = std::is_same<TO, F32>::value ? 4u : 2u;
@@ -780,6 +834,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
     __syncthreads();  // LDS reused by the next chunk
   }
 
+  const float s_fin = ldexpf(1.0f, sexp);  // S = 2^E S_reg (exact)
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
@@ -788,7 +843,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
       for (int r = 0; r < 4; ++r) {
         const int j = kkey(jt, lg, r);
         const int i = wq * IW + 16 * it + lr;
-        a.s_out[sbase + static_cast<size_t>(j) * D + i] = S[jt][it][r];
+        a.s_out[sbase + static_cast<size_t>(j) * D + i] = S[jt][it][r] * s_fin;
       }
 }
 

@@ -72,14 +72,11 @@ __device__ __forceinline__ int conv_channel(const LayerShape& L, int pc) {
 
 // W_in bf16 [hidden][n_in] -> W_in^T fp16 [n_all][hidden] in packed column
 // order (zero rows for padding).
-__global__ void pack_win_kernel(const uint16_t* __restrict__ w, LayerShape L,
-                                _Float16* __restrict__ wt) {
-  const int n_in = 2 * L.h_k * L.d + 2 * L.h_v * L.d + 2 * L.h_v;
+__global__ void pack_win_kernel(LayerShape L, _Float16* __restrict__ wt) {
   const size_t total = static_cast<size_t>(L.n_all()) * L.hidden;
   for (size_t e = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; e < total;
        e += static_cast<size_t>(gridDim.x) * blockDim.x)
     wt[e] = static_cast<_Float16>(0.0f);
-  (void)n_in;
 }
 __global__ void pack_win_copy_kernel(const uint16_t* __restrict__ w, LayerShape L,
                                      _Float16* __restrict__ wt) {
@@ -620,8 +617,7 @@ extern "C" int sr_pack_gdn_layer(const void* w_in, const void* conv_w, const voi
   _Float16* win = reinterpret_cast<_Float16*>(base);
   float* conv = reinterpret_cast<float*>(base + L.win_bytes());
   _Float16* wout = reinterpret_cast<_Float16*>(base + L.win_bytes() + L.conv_bytes());
-  hipLaunchKernelGGL(sr::pack_win_kernel, dim3(2048), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(w_in), L, win);
+  hipLaunchKernelGGL(sr::pack_win_kernel, dim3(2048), dim3(256), 0, s, L, win);
   hipLaunchKernelGGL(sr::pack_win_copy_kernel, dim3(4096), dim3(256), 0, s,
                      static_cast<const uint16_t*>(w_in), L, win);
   hipLaunchKernelGGL(sr::pack_conv_kernel, dim3(256), dim3(256), 0, s,
@@ -668,6 +664,10 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
   if ((reinterpret_cast<uintptr_t>(workspace) & (sr::kAlign - 1)) != 0) return SR_EINVAL;
   if ((reinterpret_cast<uintptr_t>(anchors) & 15u) != 0) return SR_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sr::debug_checks_enabled()) {
+    const int c = sr::check_cu_seqlens(cu_seqlens, d->n_seqs, T, s);
+    if (c != SR_OK) return c;
+  }
   char* ws = static_cast<char*>(workspace);
   float* xres = reinterpret_cast<float*>(ws + W.xres);
   float* dres = reinterpret_cast<float*>(ws + W.dres);

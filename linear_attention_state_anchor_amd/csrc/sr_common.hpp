@@ -187,6 +187,18 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 __device__ __forceinline__ float wave_sum(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_inclusive_sum(x)), kWave - 1));
 }
+// Maximum of non-negative values over the 64 lanes of a wave, returned to
+// every lane as a wave-uniform value (lanes that receive nothing from a DPP
+// step see 0, the identity for non-negative inputs).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  x = fmaxf(x, dpp_f32<0x111, 0xf>(x));  // row_shr:1
+  x = fmaxf(x, dpp_f32<0x112, 0xf>(x));  // row_shr:2
+  x = fmaxf(x, dpp_f32<0x114, 0xf>(x));  // row_shr:4
+  x = fmaxf(x, dpp_f32<0x118, 0xf>(x));  // row_shr:8
+  x = fmaxf(x, dpp_f32<0x142, 0xa>(x));  // row_bcast:15
+  x = fmaxf(x, dpp_f32<0x143, 0xc>(x));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 

@@ -13,6 +13,14 @@ Functions and the passages they follow:
   gather_suffix  -- the last k_i anchors of each hit, packed varlen
                     ("SuffixReplay", Algorithm Design 2 and Pipelined Replay
                     Path: 64-token pages, one packed variable-length batch).
+  anchor_positions, gather_anchors
+                 -- token-wise sparse anchors: each 64-token page keeps the
+                    anchors at a fixed set of in-page positions (density
+                    1/16, concentrated next to the page boundary or spread
+                    uniformly; "SuffixReplay", Algorithm Design 2, Figure 3),
+                    and the replay takes the last k_i anchors.
+  replay_budget  -- k = min(0.05 n, k_max) anchors ("SuffixReplay",
+                    Algorithm Design 3), ceil of the exact decimal ratio.
   frontend, output_path, replay_group
                  -- one replay group run from its anchors, skipping
                     full-attention layers, from a zero state, the last
@@ -150,6 +158,56 @@ def gather_suffix(pool, page_table, matched_len, suffix_len, page=64):
     packed = (np.concatenate(rows, axis=0) if rows else
               np.zeros((0, hidden), dtype=np.asarray(pool).dtype))
     return packed, cu.astype(np.int32)
+
+
+def anchor_positions(m, page_offsets, page=64):
+    """Prefix positions that hold an anchor, in increasing order, for a
+    matched prefix of m tokens whose pages keep the anchors at the in-page
+    positions page_offsets."""
+    offs = sorted(int(o) for o in page_offsets)
+    return [p * page + o for p in range((int(m) + page - 1) // page) for o in offs
+            if p * page + o < int(m)]
+
+
+def gather_anchors(pool, page_offsets, page_table, matched_len, suffix_len, page=64):
+    """Packed replay input with token-wise sparse anchors.
+
+    pool: [P][A][hidden]; block page_table[i][p] holds, in row j, request
+    i's anchor at position p*page + page_offsets[j].  Anchor a of request i
+    (counting its anchors in position order) therefore sits in block
+    page_table[i][a // A], row a % A.  The packed rows are the last k_i
+    anchors of each request.  Returns (packed [T][hidden], cu_seqlens [N+1]
+    int32, positions [T] int32).
+    """
+    pool = np.asarray(pool)
+    A = len(page_offsets)
+    rows, positions = [], []
+    cu = [0]
+    for i in range(len(matched_len)):
+        pos = anchor_positions(matched_len[i], page_offsets, page)
+        k = int(suffix_len[i])
+        if k > len(pos):
+            raise ValueError(f"request {i}: {k} anchors asked, {len(pos)} held")
+        for a in range(len(pos) - k, len(pos)):
+            rows.append(pool[page_table[i][a // A], a % A])
+            positions.append(pos[a])
+        cu.append(cu[-1] + k)
+    packed = (np.stack(rows) if rows else np.zeros((0, pool.shape[-1]), dtype=pool.dtype))
+    return packed, np.asarray(cu, dtype=np.int32), np.asarray(positions, dtype=np.int32)
+
+
+def replay_budget(n_anchors, ratio, k_max):
+    """k_i = min(ceil(ratio * n_i), k_max) with the ratio taken as the exact
+    decimal it is written as (k_max <= 0: no cap)."""
+    from fractions import Fraction
+    r = Fraction(str(ratio))
+    out = []
+    for n in n_anchors:
+        k = -((-r.numerator * int(n)) // r.denominator)   # ceil(r n), exact
+        if k_max > 0:
+            k = min(k, int(k_max))
+        out.append(int(k))
+    return out
 
 
 # ---------------------------------------------------------------------------
