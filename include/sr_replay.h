@@ -309,6 +309,28 @@ int sr_replay_group(const sr_group_desc* desc,
                     float* states, float* conv_states, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* --------------------------------------------------------------------------
+ * Allocation-free group replay, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same computation, arguments, layouts and results as
+ * sr_replay_group (bit-identical), but the workspace is a static device
+ * array of sr_replay_group_noalloc_max_bytes() bytes (256 MiB) that the
+ * library holds on every GPU it runs on until the process ends; the call
+ * allocates and frees nothing.  A group whose workspace
+ * (sr_replay_group_workspace_bytes) exceeds that size is rejected with
+ * SR_EWORKSPACE before anything is enqueued (at hidden 2560 with 16 key /
+ * 32 value heads of 128, about 3200 packed tokens fit).  All calls on one
+ * GPU share the array: calls that overlap in time on one GPU (several host
+ * threads, or several streams) race and give wrong results; serialise them.
+ * SR_EDEVICE if the array's device address cannot be obtained.
+ * ------------------------------------------------------------------------ */
+size_t sr_replay_group_noalloc_max_bytes(void);
+
+int sr_replay_group_noalloc(const sr_group_desc* desc,
+                            const sr_gdn_layer_weights* weights /* host [n_gdn] */,
+                            const void* anchors, const int32_t* cu_seqlens,
+                            float* states, float* conv_states, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

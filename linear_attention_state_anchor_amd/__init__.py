@@ -25,7 +25,8 @@ from ._lib import (ReplayArgumentError, ReplayError, SR_BF16, SR_F16, SR_F32, SR
 
 __all__ = ["gdn_replay_state", "check_replay_inputs", "gather_suffix", "gather_anchors",
            "check_gather_inputs", "replay_budget", "pack_gdn_layer", "replay_group",
-           "packed_layer_bytes", "group_workspace_bytes", "version", "ReplayError",
+           "packed_layer_bytes", "group_workspace_bytes", "replay_group_noalloc",
+           "noalloc_max_bytes", "version", "ReplayError",
            "ReplayArgumentError", "SR_LAYER_GDN", "SR_LAYER_FA", "PAGE",
            "DENSE_NEAR_BOUNDARY_1_16", "UNIFORM_1_16"]
 
@@ -322,12 +323,8 @@ def group_workspace_bytes(total_tokens, hidden, h_k, h_v, d, conv_width=4, n_seq
     return int(_lib.load().sr_replay_group_workspace_bytes(ctypes.byref(desc)))
 
 
-def replay_group(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
-                 conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None,
-                 want_conv_state=False, states=None, conv_states=None, workspace=None):
-    """Replay one group of linear-attention layers from its anchors
-    (sr_replay_group).  Returns states fp32 [n_gdn, N, h_v, d, d] (and conv
-    states fp32 [n_gdn, N, conv_dim, width-1] if asked)."""
+def _group_prepare(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width,
+                   rms_eps, l2_eps, max_seqlen, want_conv_state, states, conv_states):
     _need(anchors, "anchors", torch.bfloat16, ndim=2)
     dev = anchors.device
     _need(cu_seqlens, "cu_seqlens", torch.int32, ndim=1, device=dev)
@@ -349,18 +346,8 @@ def replay_group(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *
                              f"needs {need_bytes} (packed for another shape?)")
     if max_seqlen is None:
         max_seqlen = T
-    desc, _keep = _group_desc(kinds, hidden, h_k, h_v, d, conv_width, rms_eps, l2_eps, n, T,
-                              max_seqlen)
-    lib = _lib.load()
-    ws_bytes = int(lib.sr_replay_group_workspace_bytes(ctypes.byref(desc)))
-    if ws_bytes == 0 and n_gdn and T > 0:
-        raise ValueError("unsupported group shape")
-    if workspace is None:
-        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
-    else:
-        _need(workspace, "workspace", torch.uint8, ndim=1, device=dev)
-        if workspace.numel() < ws_bytes:
-            raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {ws_bytes}")
+    desc, keep = _group_desc(kinds, hidden, h_k, h_v, d, conv_width, rms_eps, l2_eps, n, T,
+                             max_seqlen)
     if states is None:
         states = torch.empty((n_gdn, n, h_v, d, d), dtype=torch.float32, device=dev)
     else:
@@ -375,8 +362,52 @@ def replay_group(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *
             _need(conv_states, "conv_states", torch.float32, shape, device=dev)
             conv = conv_states
     wts = (_lib.LayerWeights * max(n_gdn, 1))(*[_lib.LayerWeights(_ptr(w)) for w in packed_weights])
+    return desc, keep, wts, states, conv, n_gdn, T
+
+
+def replay_group(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
+                 conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None,
+                 want_conv_state=False, states=None, conv_states=None, workspace=None):
+    """Replay one group of linear-attention layers from its anchors
+    (sr_replay_group).  Returns states fp32 [n_gdn, N, h_v, d, d] (and conv
+    states fp32 [n_gdn, N, conv_dim, width-1] if asked)."""
+    desc, _keep, wts, states, conv, n_gdn, T = _group_prepare(
+        anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width, rms_eps,
+        l2_eps, max_seqlen, want_conv_state, states, conv_states)
+    lib = _lib.load()
+    ws_bytes = int(lib.sr_replay_group_workspace_bytes(ctypes.byref(desc)))
+    if ws_bytes == 0 and n_gdn and T > 0:
+        raise ValueError("unsupported group shape")
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=anchors.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, ndim=1, device=anchors.device)
+        if workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {ws_bytes}")
     st = lib.sr_replay_group(ctypes.byref(desc), wts, _ptr(anchors), _ptr(cu_seqlens),
                              _ptr(states), _ptr(conv), _ptr(workspace), workspace.numel(),
                              _stream())
     _lib.check("sr_replay_group", st)
+    return (states, conv) if want_conv_state else states
+
+
+def noalloc_max_bytes() -> int:
+    """Size of the static per-GPU workspace of replay_group_noalloc."""
+    return int(_lib.load().sr_replay_group_noalloc_max_bytes())
+
+
+def replay_group_noalloc(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
+                         conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None,
+                         want_conv_state=False, states=None, conv_states=None):
+    """replay_group without a workspace allocation (sr_replay_group_noalloc):
+    the library's static per-GPU workspace is used.  Pass preallocated
+    `states` (and `conv_states`) to keep the call free of allocations.
+    Calls that overlap on one GPU race."""
+    desc, _keep, wts, states, conv, n_gdn, T = _group_prepare(
+        anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width, rms_eps,
+        l2_eps, max_seqlen, want_conv_state, states, conv_states)
+    st = _lib.load().sr_replay_group_noalloc(ctypes.byref(desc), wts, _ptr(anchors),
+                                             _ptr(cu_seqlens), _ptr(states), _ptr(conv),
+                                             _stream())
+    _lib.check("sr_replay_group_noalloc", st)
     return (states, conv) if want_conv_state else states

@@ -72,6 +72,10 @@ SIGNATURES = {
     "sr_replay_group_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(GroupDesc)]),
     "sr_replay_group": (ctypes.c_int, [ctypes.POINTER(GroupDesc), ctypes.POINTER(LayerWeights),
                                        c_p, c_p, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
+    "sr_replay_group_noalloc_max_bytes": (ctypes.c_size_t, []),
+    "sr_replay_group_noalloc": (ctypes.c_int, [ctypes.POINTER(GroupDesc),
+                                               ctypes.POINTER(LayerWeights), c_p, c_p, c_p, c_p,
+                                               c_p]),
 }
 
 _lib = None

@@ -18,6 +18,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "sr_common.hpp"
@@ -634,10 +635,14 @@ extern "C" size_t sr_replay_group_workspace_bytes(const sr_group_desc* d) {
   return sr::plan(L, d->total_tokens).total;
 }
 
-extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weights* weights,
-                               const void* anchors, const int32_t* cu_seqlens, float* states,
-                               float* conv_states, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+namespace sr {
+namespace {
+
+// The whole group replay on a given workspace (shared by the entry points).
+int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights,
+                     const void* anchors, const int32_t* cu_seqlens, float* states,
+                     float* conv_states, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   if (!d || (d->n_layers > 0 && !d->layer_kind)) return SR_EINVAL;
   if (!sr::shape_ok(d) || d->n_layers < 0) return SR_ESHAPE;
   // the GDN layers must form one contiguous run; FA layers lead or trail
@@ -778,4 +783,66 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
     if (e != hipSuccess) return SR_ELAUNCH;
   }
   return SR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the workspace is a file-scope device array of
+// kScratchBytes per GPU (allocated with the code object, held until the
+// process ends).  Host code never passes the array's name to a kernel: the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current.  Every call on a GPU reuses that GPU's array, so
+// calls that overlap on one GPU race; nothing in it has to start at zero
+// (each kernel of the group writes every workspace element it later reads).
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t{256} << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+int scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SR_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return SR_EDEVICE;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SR_EDEVICE;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return SR_OK;
+}
+
+}  // namespace
+}  // namespace sr
+
+extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weights* weights,
+                               const void* anchors, const int32_t* cu_seqlens, float* states,
+                               float* conv_states, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return sr::replay_group_run(d, weights, anchors, cu_seqlens, states, conv_states, workspace,
+                              workspace_bytes, stream);
+}
+
+extern "C" size_t sr_replay_group_noalloc_max_bytes(void) { return sr::kScratchBytes; }
+
+extern "C" int sr_replay_group_noalloc(const sr_group_desc* d,
+                                       const sr_gdn_layer_weights* weights,
+                                       const void* anchors, const int32_t* cu_seqlens,
+                                       float* states, float* conv_states, void* stream) {
+  if (!d || (d->n_layers > 0 && !d->layer_kind)) return SR_EINVAL;
+  if (!sr::shape_ok(d) || d->n_layers < 0) return SR_ESHAPE;
+  // the size check comes first: a call that does not fit touches nothing
+  if (sr_replay_group_workspace_bytes(d) > sr::kScratchBytes) return SR_EWORKSPACE;
+  void* ws = nullptr;
+  const int st = sr::scratch_ptr(&ws);
+  if (st != SR_OK) return st;
+  return sr::replay_group_run(d, weights, anchors, cu_seqlens, states, conv_states, ws,
+                              sr::kScratchBytes, stream);
 }
