@@ -144,6 +144,21 @@ size_t sr_gdn_workspace_bytes(const sr_gdn_desc* desc);
 int sr_gdn_replay_state(const sr_gdn_desc* desc, const sr_gdn_io* io,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* --------------------------------------------------------------------------
+ * Single-token decode step from a reconstructed state ("Tail-Replay",
+ * section 3: the unmatched tokens continue from the reconstructed linear-
+ * attention states; "SuffixReplay", Eq. 4 for one more token).  The same
+ * recurrence and layouts as sr_gdn_replay_state with exactly one token per
+ * sequence: desc->total_tokens must equal desc->n_seqs, row n of q, k, v,
+ * alpha, beta and o belongs to sequence n, io->cu_seqlens is ignored.
+ * io->initial_state is the state before the token (NULL = 0) and
+ * io->final_state the state after it; they may be the same buffer (an
+ * in-place update).  d_k = d_v in {64, 128}; any input dtype; fp32 state
+ * arithmetic.  State buffers 8-byte aligned.  Memory-bound: each (sequence,
+ * head) state is read once and written once.
+ * ------------------------------------------------------------------------ */
+int sr_gdn_decode_step(const sr_gdn_desc* desc, const sr_gdn_io* io, void* stream);
+
 /* Validation of the device-side preconditions of one sr_gdn_replay_state
  * call (cu_seqlens, alpha, beta as described above).  Runs a kernel on
  * `stream`, waits for it and returns SR_OK, SR_EDATA, or the host-side
@@ -308,6 +323,35 @@ int sr_replay_group(const sr_group_desc* desc,
                     const void* anchors, const int32_t* cu_seqlens,
                     float* states, float* conv_states, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Continuation of a group from reconstructed states ("Tail-Replay",
+ * section 3: the unmatched tokens continue from the reconstructed linear-
+ * attention states; "SuffixReplay", System Design: replay and extend hand
+ * over at group boundaries).  The new tokens of each sequence run through
+ * the group's GDN layers as in sr_replay_group, but every layer starts from
+ * its given state and short-conv window instead of zero:
+ *   tokens               [T][hidden] bf16, the group input of the new tokens
+ *   initial_states       [n_gdn][n_seqs][h_v][d][d] fp32 or NULL (= 0), the
+ *                        layout sr_replay_group writes
+ *   initial_conv_states  [n_gdn][n_seqs][conv_dim][conv_width-1] fp32 or
+ *                        NULL (= zero history), the layout it writes
+ *   states, conv_states  outputs as for sr_replay_group (conv_states may be
+ *                        NULL); they must not alias the initial ones
+ *   hidden_out           [T][hidden] fp32 or NULL: the group's output hidden
+ *                        states (the last layer's residual plus its mixer
+ *                        output; asking for it makes the last layer compute
+ *                        its full mixer)
+ * Workspace, errors and supported shapes as for sr_replay_group.  Replaying
+ * a prefix and extending it by the rest equals replaying the whole sequence
+ * up to rounding (chunk boundaries differ).
+ * ------------------------------------------------------------------------ */
+int sr_extend_group(const sr_group_desc* desc,
+                    const sr_gdn_layer_weights* weights /* host [n_gdn] */,
+                    const void* tokens, const int32_t* cu_seqlens,
+                    const float* initial_states, const float* initial_conv_states,
+                    float* states, float* conv_states, float* hidden_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
  * Allocation-free group replay, for callers that cannot allocate device

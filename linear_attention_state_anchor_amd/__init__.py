@@ -23,7 +23,8 @@ from . import _lib
 from ._lib import (ReplayArgumentError, ReplayError, SR_BF16, SR_F16, SR_F32, SR_LAYER_FA,
                    SR_LAYER_GDN)
 
-__all__ = ["gdn_replay_state", "check_replay_inputs", "gather_suffix", "gather_anchors",
+__all__ = ["gdn_replay_state", "gdn_decode_step", "extend_group", "check_replay_inputs",
+           "gather_suffix", "gather_anchors",
            "check_gather_inputs", "replay_budget", "pack_gdn_layer", "replay_group",
            "packed_layer_bytes", "group_workspace_bytes", "replay_group_noalloc",
            "noalloc_max_bytes", "version", "ReplayError",
@@ -142,6 +143,29 @@ def gdn_replay_state(q, k, v, alpha, beta=None, cu_seqlens=None, initial_state=N
                                  _stream())
     _lib.check("sr_gdn_replay_state", st)
     return final_state, o
+
+
+def gdn_decode_step(q, k, v, alpha, beta=None, state=None, *, erase=True, alpha_is_log=False,
+                    scale=1.0, want_o=True, o_dtype=None, out_state=None, o=None):
+    """One decode token per sequence from a given state (sr_gdn_decode_step).
+
+    q, k: [N, h_k, d]; v: [N, h_v, d] (row n: sequence n's token); alpha,
+    beta: [N, h_v] fp32; state: fp32 [N, h_v, d, d] (the state before the
+    token, transposed as gdn_replay_state returns it) or None (= 0).
+    out_state may be `state` itself for an in-place update (the default when
+    a state is given).  Returns (state after the token, o [N, h_v, d] or None).
+    """
+    _need(k, "k", ndim=3)
+    N = k.shape[0]
+    cu_dummy = torch.zeros((N + 1,), dtype=torch.int32, device=k.device)
+    if out_state is None:
+        out_state = state
+    desc, io, out_state, o = _gdn_call(q, k, v, alpha, beta, cu_dummy, state, erase,
+                                       alpha_is_log, scale, want_o, o_dtype, out_state, o)
+    io.cu_seqlens = None
+    st = _lib.load().sr_gdn_decode_step(ctypes.byref(desc), ctypes.byref(io), _stream())
+    _lib.check("sr_gdn_decode_step", st)
+    return out_state, o
 
 
 def check_replay_inputs(q, k, v, alpha, beta=None, cu_seqlens=None, initial_state=None, *,
@@ -411,3 +435,45 @@ def replay_group_noalloc(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h
                                              _stream())
     _lib.check("sr_replay_group_noalloc", st)
     return (states, conv) if want_conv_state else states
+
+
+def extend_group(tokens, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
+                 initial_states=None, initial_conv_states=None, want_hidden=True,
+                 conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None, states=None,
+                 conv_states=None, workspace=None):
+    """Continue a group from given per-layer states and conv windows over new
+    tokens (sr_extend_group).  Returns (states, conv_states, hidden_out fp32
+    [T, hidden] or None)."""
+    desc, _keep, wts, states, conv, n_gdn, T = _group_prepare(
+        tokens, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width, rms_eps,
+        l2_eps, max_seqlen, True, states, conv_states)
+    dev = tokens.device
+    n = cu_seqlens.shape[0] - 1
+    if initial_states is not None:
+        _need(initial_states, "initial_states", torch.float32, (n_gdn, n, h_v, d, d), device=dev)
+        if initial_states.data_ptr() == states.data_ptr():
+            raise ValueError("states must not alias initial_states")
+    if initial_conv_states is not None:
+        _need(initial_conv_states, "initial_conv_states", torch.float32, tuple(conv.shape),
+              device=dev)
+        if initial_conv_states.data_ptr() == conv.data_ptr():
+            raise ValueError("conv_states must not alias initial_conv_states")
+    hidden = None
+    if want_hidden:
+        hidden = torch.empty((T, tokens.shape[1]), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    ws_bytes = int(lib.sr_replay_group_workspace_bytes(ctypes.byref(desc)))
+    if ws_bytes == 0 and n_gdn and T > 0:
+        raise ValueError("unsupported group shape")
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, ndim=1, device=dev)
+        if workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, needs {ws_bytes}")
+    st = lib.sr_extend_group(ctypes.byref(desc), wts, _ptr(tokens), _ptr(cu_seqlens),
+                             _ptr(initial_states), _ptr(initial_conv_states), _ptr(states),
+                             _ptr(conv), _ptr(hidden), _ptr(workspace), workspace.numel(),
+                             _stream())
+    _lib.check("sr_extend_group", st)
+    return states, conv, hidden

@@ -57,6 +57,7 @@ SIGNATURES = {
                                            ctypes.c_size_t, c_p]),
     "sr_check_replay_inputs": (ctypes.c_int, [ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnIO),
                                               c_p]),
+    "sr_gdn_decode_step": (ctypes.c_int, [ctypes.POINTER(GdnDesc), ctypes.POINTER(GdnIO), c_p]),
     "sr_gather_suffix": (ctypes.c_int, [c_p, c_i32, c_i32, ctypes.c_int64, c_p, c_i32, c_p,
                                         c_p, c_i32, c_i32, c_p, c_p, c_p]),
     "sr_gather_anchors": (ctypes.c_int, [c_p, c_i32, c_i32, ctypes.c_int64, c_i32,
@@ -72,6 +73,9 @@ SIGNATURES = {
     "sr_replay_group_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(GroupDesc)]),
     "sr_replay_group": (ctypes.c_int, [ctypes.POINTER(GroupDesc), ctypes.POINTER(LayerWeights),
                                        c_p, c_p, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
+    "sr_extend_group": (ctypes.c_int, [ctypes.POINTER(GroupDesc), ctypes.POINTER(LayerWeights),
+                                       c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, ctypes.c_size_t,
+                                       c_p]),
     "sr_replay_group_noalloc_max_bytes": (ctypes.c_size_t, []),
     "sr_replay_group_noalloc": (ctypes.c_int, [ctypes.POINTER(GroupDesc),
                                                ctypes.POINTER(LayerWeights), c_p, c_p, c_p, c_p,

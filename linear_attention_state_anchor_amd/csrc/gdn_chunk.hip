@@ -26,8 +26,11 @@
 // products.
 //
 // Work layout: a workgroup holds HP value heads that share a key head, NW
-// waves per head, and walks one sequence's chunks in order; wave w of a head
-// owns value columns [w*D/NW, (w+1)*D/NW) (the launch picks HP and NW from
+// waves per head, and walks one sequence's chunks in order; it owns the
+// value columns [c0, c0 + D/VS) of its heads (VS = 1, or 2 when a launch has
+// too few chains to fill the CUs: value columns of S evolve independently,
+// so the split is exact and only the key-side tiles are formed twice), and
+// wave w of a head owns D/VS/NW of them (the launch picks HP, NW and VS from
 // the number of (sequence, head) chains).  The transposed state S^T
 // (d_k x d_v, fp32) stays in accumulator registers for the whole sequence.
 // Accumulator tiles feed later products directly as operands: two
@@ -55,6 +58,8 @@ constexpr int kC = 64;         // chunk length (tokens)
 //    both heads; one workgroup of 8 waves per CU;
 //  * HP = 1, NW = 8 for at most one chain per CU: 16 value columns per
 //    wave, two waves per SIMD instead of one;
+//  * HP = 1, NW = 4, VS = 2 for at most half a chain per CU: two workgroups
+//    per chain, 16 value columns per wave;
 //  * HP = 1, NW = 4 otherwise: two workgroups of 4 waves per CU.
 constexpr int kAS = kC + 8;    // fp16 row stride of -A
 constexpr int kPS = kC + 8;    // fp16 row stride of P o QK^T
@@ -358,17 +363,19 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
   }
 }
 
-template <int D, typename TI, typename TO, bool ERASE, bool WANT_O, int HP, int NW>
+template <int D, typename TI, typename TO, bool ERASE, bool WANT_O, int HP, int NW, int VS>
 __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_kernel(
     GdnArgs a, int units_per_xcd) {
   constexpr int kThreads = 64 * NW * HP;
-  constexpr int IW = D / NW;      // value columns per wave
+  constexpr int DV = D / VS;      // value columns of the workgroup (per head)
+  constexpr int IW = DV / NW;     // value columns per wave
   constexpr int NIT = IW / 16;    // 16-wide column tiles per wave
   constexpr int NJT = D / 16;     // 16-wide key tiles
   constexpr int NKJ = D / 32;     // K = 32 steps over the key dimension
   constexpr int CPR = D / 8;      // 16-byte chunks per row
   constexpr int NPF = kC * CPR / kThreads;  // 16-byte K (and Q) row pieces per thread
-  constexpr int VCP = CPR * HP;             // 16-byte V pieces per token row (all heads)
+  constexpr int VCPH = CPR / VS;            // 16-byte V pieces per token row and head
+  constexpr int VCP = VCPH * HP;            // 16-byte V pieces per token row (all heads)
   constexpr int NPFV = kC * VCP / kThreads; // V pieces per thread
   constexpr int kWS = ChunkSmem<D, HP>::kWS;
   static_assert(NIT >= 1 && IW % 16 == 0, "D too small");
@@ -380,11 +387,14 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
   // XCD-aware numbering: consecutive (sequence, head group) units share an
   // XCD (with one head per workgroup, the value heads of a key head then
   // read K and Q through one L2).
+  // (with VS > 1 the VS column slices of one chain are consecutive units, so
+  // they share an XCD and read the chain's K and Q through one L2)
   const int unit = (blockIdx.x % kXcd) * units_per_xcd + blockIdx.x / kXcd;
   const int groups = a.h_v / HP;  // head groups per sequence
-  if (unit >= a.n_seqs * groups) return;  // padding workgroup
-  const int n = unit / groups;
-  const int hb = (unit % groups) * HP;    // first value head of the workgroup
+  if (unit >= a.n_seqs * groups * VS) return;  // padding workgroup
+  const int n = unit / (groups * VS);
+  const int hb = ((unit / VS) % groups) * HP;  // first value head of the workgroup
+  const int col0 = (unit % VS) * DV;           // first value column of the workgroup
   const int g = hb / (a.h_v / a.h_k);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
@@ -398,7 +408,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
   const uint16_t* qg = want_o ? static_cast<const uint16_t*>(a.q) + static_cast<size_t>(g) * D
                               : nullptr;
   // V rows of the workgroup's heads (adjacent in each token row)
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(hb) * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + static_cast<size_t>(hb) * D + col0;
 
   // S^T accumulators: tile (jt, it) = 16 key rows, value columns
   // w*IW + 16it..; lane holds column lr and the keys kkey(jt, lg, 0..3).
@@ -412,7 +422,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = kkey(jt, lg, r);
-        const int i = wq * IW + 16 * it + lr;
+        const int i = col0 + wq * IW + 16 * it + lr;
         S[jt][it][r] = a.s0 ? a.s0[sbase + static_cast<size_t>(j) * D + i] : 0.0f;
       }
   // Retire the initial-state loads here: otherwise the compiler's wait
@@ -446,7 +456,11 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
   // V: this thread's piece of a token row of all the workgroup's heads
   auto v_lane_row = [&]() { return (static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) / VCP; };
   auto v_lane_piece = [&]() { return (static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) % VCP; };
-  auto v_off = [&]() { return 2u * (v_lane_row() * static_cast<unsigned>(v_row) + 8u * v_lane_piece()); };
+  auto v_off = [&]() {
+    const unsigned cp = v_lane_piece();
+    return 2u * (v_lane_row() * static_cast<unsigned>(v_row) + static_cast<unsigned>(D) * (cp / VCPH) +
+                 8u * (cp % VCPH));
+  };
   // One 16-byte piece e of the next chunk's K, Q or V rows per thread (zero
   // past the end of the sequence), and the next chunk's gates (wave 0).
   auto pf_k = [&](int e, int c0n) {
@@ -560,7 +574,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
 #pragma unroll
     for (int e = 0; e < NPFV; ++e) {
       const unsigned row = v_lane_row() + (kThreads / VCP) * e, cp = v_lane_piece();
-      lds_store16(lds_addr(&sm.w[cp / CPR][0]) + 2 * (row * kWS + 8 * (cp % CPR)), pv[e]);
+      lds_store16(lds_addr(&sm.w[cp / VCPH][0]) + 2 * (row * kWS + col0 + 8 * (cp % VCPH)), pv[e]);
     }
     if (wq == 0) {
       sm.gcum[hp][l] = n_g;
@@ -643,7 +657,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
 #pragma unroll
       for (int it = 0; it < NIT; ++it) S16[kk][it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
     // transpose-read base of this lane in the V tile at this wave's columns
-    const uint32_t xv = tr_base(lds_addr(&sm.w[hp][0]) + 2 * (wq * IW + trv));
+    const uint32_t xv = tr_base(lds_addr(&sm.w[hp][0]) + 2 * (col0 + wq * IW + trv));
     if (ERASE) {
       // ---- right-hand side R~ = V - diag(e^G) K S^T ------------------------
       // K S^T for this wave's value columns, one key k-step at a time: S^T
@@ -800,7 +814,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
             constexpr unsigned kOB = std::is_same<TO, F32>::value ? 4u : 2u;
             char* ob0 = static_cast<char*>(a.o) + (static_cast<size_t>(c0) * a.h_v + h) * D * kOB;
             const unsigned oo = kOB * (static_cast<unsigned>(t) * static_cast<unsigned>(a.h_v) * D +
-                                       static_cast<unsigned>(wq * IW + 4 * lg));
+                                       static_cast<unsigned>(col0 + wq * IW + 4 * lg));
 #pragma unroll
             for (int it = 0; it < NIT; ++it) store4<TO>(ob0 + oo + kOB * 16 * it, 0, O[u][it]);
           }
@@ -842,42 +856,49 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = kkey(jt, lg, r);
-        const int i = wq * IW + 16 * it + lr;
+        const int i = col0 + wq * IW + 16 * it + lr;
         a.s_out[sbase + static_cast<size_t>(j) * D + i] = S[jt][it][r] * s_fin;
       }
 }
 
-template <int D, typename TI, typename TO, int HP, int NW>
+template <int D, typename TI, typename TO, int HP, int NW, int VS>
 hipError_t launch4(const GdnArgs& a, hipStream_t s) {
-  const int units = a.n_seqs * (a.h_v / HP);
+  const int units = a.n_seqs * (a.h_v / HP) * VS;
   const int per_xcd = (units + kXcd - 1) / kXcd;
   dim3 grid(per_xcd * kXcd), block(64 * NW * HP);
   const bool o = a.o != nullptr;
   if (a.erase && o)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true, HP, NW>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true, HP, NW, VS>), grid, block, 0, s, a, per_xcd);
   else if (a.erase)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, false, HP, NW>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, false, HP, NW, VS>), grid, block, 0, s, a, per_xcd);
   else if (o)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, true, HP, NW>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, true, HP, NW, VS>), grid, block, 0, s, a, per_xcd);
   else
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, false, HP, NW>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, false, HP, NW, VS>), grid, block, 0, s, a, per_xcd);
   return hipGetLastError();
 }
 
-// Launch shape by the number of (sequence, value head) chains: two value
-// heads per workgroup where the value heads of a key head pair up and there
-// are at least two chains per compute unit; 8 waves on one head for at most
-// one chain per CU; otherwise one head of 4 waves.  (For 4 x 32 chains the
-// pair layout measured 184 us against 141 us for one head of 4 waves.)
+// Launch shape by the number of (sequence, value head) chains:
+//  * two value heads per workgroup where the value heads of a key head pair
+//    up and there are at least two chains per compute unit;
+//  * at most half a chain per CU (d = 128): each chain's value columns split
+//    over two workgroups of 4 waves (the key-side tiles are formed by both),
+//    so the launch fills the CUs (4 x 32 chains: 118 instead of 128 us with
+//    outputs, 87 instead of 102 us state-only);
+//  * up to one chain per CU (d = 128): one head of 8 waves (16 value columns
+//    per wave, two waves per SIMD); the two-workgroup split measured slower
+//    here (8 x 32 chains, scalar decay: 168 against 146 us);
+//  * otherwise one head of 4 waves.
 constexpr int kGfx950Cus = 256;  // compute units of the gfx950 parts (MI350X, MI355X)
 template <int D, typename TI, typename TO>
 hipError_t launch3(const GdnArgs& a, hipStream_t s) {
   const int chains = a.n_seqs * a.h_v;
-  if ((a.h_v / a.h_k) % 2 == 0 && chains >= 2 * kGfx950Cus) return launch4<D, TI, TO, 2, 4>(a, s);
+  if ((a.h_v / a.h_k) % 2 == 0 && chains >= 2 * kGfx950Cus) return launch4<D, TI, TO, 2, 4, 1>(a, s);
   if constexpr (D == 128) {  // 16 value columns per wave (d = 64 would leave 8)
-    if (chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 8>(a, s);
+    if (2 * chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 4, 2>(a, s);
+    if (chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 8, 1>(a, s);
   }
-  return launch4<D, TI, TO, 1, 4>(a, s);
+  return launch4<D, TI, TO, 1, 4, 1>(a, s);
 }
 
 template <int D, typename TI>

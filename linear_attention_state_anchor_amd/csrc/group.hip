@@ -378,10 +378,15 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
 constexpr int FT = 64;  // tokens per workgroup
 
 // MAXW: conv widths up to MAXW (4 or 8); SiLU uses the hardware reciprocal
+// conv0 (may be null): per sequence the last width-1 pre-conv rows before
+// its first token ([n][conv_dim][width-1], original q|k|v channel order,
+// oldest first), used for the taps that reach before the sequence start
+// (continuation from a reconstructed state); null means zero history.
 template <int D, int MAXW>
 __global__ __launch_bounds__(256) void frontend_kernel(
     const _Float16* __restrict__ P, int ldp, LayerShape L, const float* __restrict__ convw,
-    const int32_t* __restrict__ seq_start, int T, float l2_eps, int n_conv_heads,
+    const int32_t* __restrict__ seq_start, const int32_t* __restrict__ seq_id,
+    const float* __restrict__ conv0, int T, float l2_eps, int n_conv_heads,
     _Float16* __restrict__ qo, _Float16* __restrict__ ko, _Float16* __restrict__ vo,
     float* __restrict__ la, float* __restrict__ be) {
   constexpr int CPL = D / kWave;  // channels per lane
@@ -398,14 +403,14 @@ __global__ __launch_bounds__(256) void frontend_kernel(
     }
     return;
   }
-  int kind, hidx, pc0, nh;  // kind 0: k, 1: v, 2: q
+  int kind, hidx, pc0, nh, oc0;  // kind 0: k, 1: v, 2: q; oc0: original channel
   _Float16* out;
   if (hh < nk) {
-    kind = 0; hidx = hh; pc0 = hh * D; nh = nk; out = ko;
+    kind = 0; hidx = hh; pc0 = hh * D; nh = nk; out = ko; oc0 = (nk + hidx) * D;
   } else if (hh < nk + nv) {
-    kind = 1; hidx = hh - nk; pc0 = nk * D + hidx * D; nh = nv; out = vo;
+    kind = 1; hidx = hh - nk; pc0 = nk * D + hidx * D; nh = nv; out = vo; oc0 = (2 * nk + hidx) * D;
   } else {
-    kind = 2; hidx = hh - nk - nv; pc0 = L.q_off() + hidx * D; nh = nk; out = qo;
+    kind = 2; hidx = hh - nk - nv; pc0 = L.q_off() + hidx * D; nh = nk; out = qo; oc0 = hidx * D;
   }
   const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int c0 = CPL * lane;
@@ -427,8 +432,11 @@ __global__ __launch_bounds__(256) void frontend_kernel(
     const bool ok = row >= 0 && row < T && r >= MAXW - W;
     u[r] = ok ? *reinterpret_cast<const h2*>(P + static_cast<size_t>(row) * ldp + pc0 + c0) : h2{};
   }
-  // sequence starts of the wave's 16 tokens, one per lane (broadcast below)
+  // sequence starts (and ids) of the wave's 16 tokens, one per lane
+  // (broadcast below)
   const int sq = seq_start[min(tb + lane % 16, T - 1)];
+  const int sid = conv0 ? seq_id[min(tb + lane % 16, T - 1)] : 0;
+  const int W1 = W - 1;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int t = tb + i;
@@ -439,8 +447,18 @@ __global__ __launch_bounds__(256) void frontend_kernel(
     for (int e = 0; e < CPL; ++e) {
       float acc = 0.0f;
 #pragma unroll
-      for (int k = 0; k < MAXW; ++k)  // row t-k is u[MAXW-1+i-k]
-        if (k <= back) acc = fmaf(wt[e][k], static_cast<float>(u[MAXW - 1 + i - k][e]), acc);
+      for (int k = 0; k < MAXW; ++k) {  // row t-k is u[MAXW-1+i-k]
+        if (k <= back) {
+          acc = fmaf(wt[e][k], static_cast<float>(u[MAXW - 1 + i - k][e]), acc);
+        } else if (conv0 && k < W && back >= 0) {
+          // row t-k lies k-back rows before the sequence start: entry
+          // W-1-(k-back) of the carried-in window
+          const int n = __builtin_amdgcn_readlane(sid, i);
+          acc = fmaf(wt[e][k],
+                     conv0[(static_cast<size_t>(n) * L.conv_dim() + oc0 + c0 + e) * W1 + (W1 - (k - back))],
+                     acc);
+        }
+      }
       y[e] = acc * __builtin_amdgcn_rcpf(1.0f + __expf(-acc));  // SiLU
       ss = fmaf(y[e], y[e], ss);
     }
@@ -460,9 +478,11 @@ __global__ __launch_bounds__(256) void frontend_kernel(
 
 // conv state: last W-1 pre-conv rows of q|k|v per sequence (original
 // channel order), oldest first, zero where the sequence is shorter
+// (rows before the sequence start come from the carried-in window conv0,
+// or are zero without one)
 __global__ void conv_state_kernel(const _Float16* __restrict__ P, int ldp, LayerShape L,
                                   const int32_t* __restrict__ cu, int n_seqs,
-                                  float* __restrict__ out) {
+                                  const float* __restrict__ conv0, float* __restrict__ out) {
   const int n = blockIdx.y;
   const int W1 = L.width - 1;
   const int cd = L.conv_dim();
@@ -471,9 +491,18 @@ __global__ void conv_state_kernel(const _Float16* __restrict__ P, int ldp, Layer
     const int start = cu[n], end = cu[n + 1];
     const int pos = end - W1 + j;
     float v = 0.0f;
-    if (pos >= start) v = static_cast<float>(P[static_cast<size_t>(pos) * ldp + L.packed_col(c)]);
+    if (pos >= start)
+      v = static_cast<float>(P[static_cast<size_t>(pos) * ldp + L.packed_col(c)]);
+    else if (conv0)
+      v = conv0[(static_cast<size_t>(n) * cd + c) * W1 + (W1 - (start - pos))];
     out[(static_cast<size_t>(n) * cd + c) * W1 + j] = v;
   }
+}
+
+__global__ void copy_kernel(const float* __restrict__ src, float* __restrict__ dst, size_t n) {
+  for (size_t e = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; e < n;
+       e += static_cast<size_t>(gridDim.x) * blockDim.x)
+    dst[e] = src[e];
 }
 
 __global__ void fill_kernel(float* __restrict__ p, size_t n, float v) {
@@ -482,9 +511,9 @@ __global__ void fill_kernel(float* __restrict__ p, size_t n, float v) {
     p[e] = v;
 }
 
-// seq_start[t] = cu[n] for the sequence n holding token t
+// seq_start[t] = cu[n] and seq_id[t] = n for the sequence n holding token t
 __global__ void seq_start_kernel(const int32_t* __restrict__ cu, int n_seqs, int T,
-                                 int32_t* __restrict__ out) {
+                                 int32_t* __restrict__ out, int32_t* __restrict__ ids) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   int lo = 0, hi = n_seqs - 1;
@@ -494,6 +523,17 @@ __global__ void seq_start_kernel(const int32_t* __restrict__ cu, int n_seqs, int
     else hi = mid - 1;
   }
   out[t] = cu[lo];
+  ids[t] = lo;
+}
+
+// out = x + dlt (the group's output hidden state: the last layer's residual
+// stream plus its output projection), fp32
+template <typename TX>
+__global__ __launch_bounds__(256) void residual_out_kernel(const void* x, const float* __restrict__ dlt,
+                                                           size_t count, float* __restrict__ out) {
+  for (size_t e = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; e < count;
+       e += static_cast<size_t>(gridDim.x) * blockDim.x)
+    out[e] = load1<TX>(x, e) + dlt[e];
 }
 
 // y = o / sqrt(mean(o^2) + eps) * SiLU(z), per (token, value head), fp16 out;
@@ -535,7 +575,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(const _Float16* __restr
 // workspace layout of one group call
 // ---------------------------------------------------------------------------
 struct Workspace {
-  size_t xres, dres, xh, p, q, k, v, la, be, o, y, ss, total;
+  size_t xres, dres, xh, p, q, k, v, la, be, o, y, ss, sid, total;
 };
 
 Workspace plan(const LayerShape& L, int T) {
@@ -559,6 +599,7 @@ Workspace plan(const LayerShape& L, int T) {
   w.o = take(t * L.h_v * L.d * 2);
   w.y = take(t * L.h_v * L.d * 2);
   w.ss = take(t * 4);
+  w.sid = take(t * 4);
   w.total = off;
   return w;
 }
@@ -639,10 +680,13 @@ namespace sr {
 namespace {
 
 // The whole group replay on a given workspace (shared by the entry points).
+// states0 / conv0 (may be null): per-layer states and conv windows to start
+// from (continuation); hidden_out (may be null): the group's output hidden
+// states, which makes the last layer run its full mixer as well.
 int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights,
-                     const void* anchors, const int32_t* cu_seqlens, float* states,
-                     float* conv_states, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+                     const void* anchors, const int32_t* cu_seqlens, const float* states0,
+                     const float* conv0, float* states, float* conv_states, float* hidden_out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   if (!d || (d->n_layers > 0 && !d->layer_kind)) return SR_EINVAL;
   if (!sr::shape_ok(d) || d->n_layers < 0) return SR_ESHAPE;
   // the GDN layers must form one contiguous run; FA layers lead or trail
@@ -686,16 +730,21 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
   _Float16* ob = reinterpret_cast<_Float16*>(ws + W.o);
   _Float16* yb = reinterpret_cast<_Float16*>(ws + W.y);
   int32_t* sst = reinterpret_cast<int32_t*>(ws + W.ss);
+  int32_t* sid = reinterpret_cast<int32_t*>(ws + W.sid);
   const size_t state_stride = static_cast<size_t>(d->n_seqs) * d->h_v * d->d * d->d;
   const size_t conv_stride = static_cast<size_t>(d->n_seqs) * L.conv_dim() * (L.width - 1);
 
   if (T > 0) {
     hipLaunchKernelGGL(sr::seq_start_kernel, dim3((T + 255) / 256), dim3(256), 0, s, cu_seqlens,
-                       d->n_seqs, T, sst);
+                       d->n_seqs, T, sst, sid);
     if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
   }
   for (int li = 0; li < n_gdn; ++li) {
     const bool is_last = li == n_gdn - 1;
+    // the mixer's outputs are formed for every layer but the last, and for
+    // the last too when the group's output is asked for
+    const bool full = !is_last || hidden_out != nullptr;
+    const float* lconv0 = conv0 ? conv0 + conv_stride * li : nullptr;
     const char* pk = static_cast<const char*>(weights[li].packed);
     const _Float16* win = reinterpret_cast<const _Float16*>(pk);
     const float* convw = reinterpret_cast<const float*>(pk + L.win_bytes());
@@ -719,30 +768,34 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
       if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
       // the last layer needs k|v|a|b for its state, and q as well when its
       // conv window is returned (q follows the state prefix in the packing)
-      const int N = !is_last ? L.n_all()
+      const int N = full ? L.n_all()
                   : conv_states ? static_cast<int>(sr::align_up(L.q_off() + d->h_k * d->d, 128))
                                 : L.n_state_pad();
       if (sr::gemm<sr::EPI_STORE16>(xh, d->hidden, win, d->hidden, T, N, d->hidden, P, L.n_all(),
                                     s) != hipSuccess)
         return SR_ELAUNCH;
       // conv heads: k, v (and q unless this is the last layer), then gates
-      const int n_conv = is_last ? d->h_k + d->h_v : 2 * d->h_k + d->h_v;
+      const int n_conv = full ? 2 * d->h_k + d->h_v : d->h_k + d->h_v;
       const dim3 fgrid((T + sr::FT - 1) / sr::FT, n_conv + 1);
       auto fe = d->d == 128 ? (L.width <= 4 ? sr::frontend_kernel<128, 4> : sr::frontend_kernel<128, 8>)
                             : (L.width <= 4 ? sr::frontend_kernel<64, 4> : sr::frontend_kernel<64, 8>);
-      hipLaunchKernelGGL(fe, fgrid, dim3(256), 0, s, P, L.n_all(), L, convw, sst, T, d->l2_eps,
-                         n_conv, qb, kb, vb, la, be);
+      hipLaunchKernelGGL(fe, fgrid, dim3(256), 0, s, P, L.n_all(), L, convw, sst, sid, lconv0, T,
+                         d->l2_eps, n_conv, qb, kb, vb, la, be);
       if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
       if (conv_states) {
         hipLaunchKernelGGL(sr::conv_state_kernel, dim3(64, d->n_seqs), dim3(256), 0, s, P, L.n_all(),
-                           L, cu_seqlens, d->n_seqs, conv_states + conv_stride * li);
+                           L, cu_seqlens, d->n_seqs, lconv0, conv_states + conv_stride * li);
         if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
       }
     } else if (conv_states) {
-      // no replayed tokens: the conv windows are empty (a fill kernel, not a
-      // memset, so the call stays safe to capture in a graph)
-      hipLaunchKernelGGL(sr::fill_kernel, dim3(256), dim3(256), 0, s,
-                         conv_states + conv_stride * li, conv_stride, 0.0f);
+      // no tokens: the conv windows are the carried-in ones, or empty (kernels,
+      // not memset/memcpy nodes, so the call stays safe to capture in a graph)
+      if (lconv0)
+        hipLaunchKernelGGL(sr::copy_kernel, dim3(256), dim3(256), 0, s, lconv0,
+                           conv_states + conv_stride * li, conv_stride);
+      else
+        hipLaunchKernelGGL(sr::fill_kernel, dim3(256), dim3(256), 0, s,
+                           conv_states + conv_stride * li, conv_stride, 0.0f);
       if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
     }
     sr::GdnArgs g{};
@@ -757,17 +810,17 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
     g.erase = 1;
     g.alpha_is_log = 1;
     g.scale = 1.0f;
-    g.q = is_last ? nullptr : qb;
+    g.q = full ? qb : nullptr;
     g.k = kb;
     g.v = vb;
     g.alpha = la;
     g.beta = be;
     g.cu = cu_seqlens;
-    g.s0 = nullptr;
+    g.s0 = states0 ? states0 + state_stride * li : nullptr;
     g.s_out = st;
-    g.o = is_last ? nullptr : ob;
+    g.o = full ? ob : nullptr;
     if (sr::launch_gdn_chunk(g, s) != hipSuccess) return SR_ELAUNCH;
-    if (is_last || T == 0) continue;
+    if (!full || T == 0) continue;
     const int rows = T * d->h_v;
     const dim3 ngrid((rows + 15) / 16);
     if (d->d == 128)
@@ -781,6 +834,18 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
     // the residual add happens in the next layer's RMSNorm
     hipError_t e = sr::gemm<sr::EPI_STORE32>(yb, K2, wout, K2, T, d->hidden, K2, dres, d->hidden, s);
     if (e != hipSuccess) return SR_ELAUNCH;
+    if (is_last) {
+      // the group's output: the last layer's input plus its mixer output
+      const size_t count = static_cast<size_t>(T) * d->hidden;
+      const int blocks = static_cast<int>(std::min<size_t>(4096, (count + 255) / 256));
+      if (li == 0)
+        hipLaunchKernelGGL(sr::residual_out_kernel<sr::BF16>, dim3(blocks), dim3(256), 0, s, anchors,
+                           dres, count, hidden_out);
+      else
+        hipLaunchKernelGGL(sr::residual_out_kernel<sr::F32>, dim3(blocks), dim3(256), 0, s,
+                           static_cast<const void*>(xres), dres, count, hidden_out);
+      if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+    }
   }
   return SR_OK;
 }
@@ -826,7 +891,17 @@ extern "C" int sr_replay_group(const sr_group_desc* d, const sr_gdn_layer_weight
                                const void* anchors, const int32_t* cu_seqlens, float* states,
                                float* conv_states, void* workspace, size_t workspace_bytes,
                                void* stream) {
-  return sr::replay_group_run(d, weights, anchors, cu_seqlens, states, conv_states, workspace,
+  return sr::replay_group_run(d, weights, anchors, cu_seqlens, nullptr, nullptr, states,
+                              conv_states, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" int sr_extend_group(const sr_group_desc* d, const sr_gdn_layer_weights* weights,
+                               const void* tokens, const int32_t* cu_seqlens,
+                               const float* initial_states, const float* initial_conv_states,
+                               float* states, float* conv_states, float* hidden_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return sr::replay_group_run(d, weights, tokens, cu_seqlens, initial_states,
+                              initial_conv_states, states, conv_states, hidden_out, workspace,
                               workspace_bytes, stream);
 }
 
@@ -843,6 +918,6 @@ extern "C" int sr_replay_group_noalloc(const sr_group_desc* d,
   void* ws = nullptr;
   const int st = sr::scratch_ptr(&ws);
   if (st != SR_OK) return st;
-  return sr::replay_group_run(d, weights, anchors, cu_seqlens, states, conv_states, ws,
-                              sr::kScratchBytes, stream);
+  return sr::replay_group_run(d, weights, anchors, cu_seqlens, nullptr, nullptr, states,
+                              conv_states, nullptr, ws, sr::kScratchBytes, stream);
 }

@@ -237,13 +237,14 @@ def sigmoid(x):
         return 1.0 / (1.0 + np.exp(-x))
 
 
-def causal_conv_silu(u, conv_w, cu_seqlens):
+def causal_conv_silu(u, conv_w, cu_seqlens, initial_state=None):
     """Depthwise causal conv per sequence, then SiLU.
 
-    y_t[c] = SiLU(sum_j w[c][j] * u_{t-W+1+j}[c]), with u = 0 before each
-    sequence start (replay starts from an empty history) and tap W-1 on the
-    current token.  Returns (y, conv_state [N][C][W-1]: the last W-1 rows of u
-    per sequence, oldest first, zero where the sequence is shorter).
+    y_t[c] = SiLU(sum_j w[c][j] * u_{t-W+1+j}[c]), with tap W-1 on the
+    current token and, before each sequence start, the W-1 rows of
+    initial_state [N][C][W-1] (oldest first) -- zeros when it is None, the
+    replay case (an empty history).  Returns (y, conv_state [N][C][W-1]: the
+    last W-1 rows of the history followed by the sequence, oldest first).
     """
     u = np.asarray(u, dtype=np.float64)
     w = np.asarray(conv_w, dtype=np.float64)
@@ -254,7 +255,9 @@ def causal_conv_silu(u, conv_w, cu_seqlens):
     state = np.zeros((n, u.shape[1], W - 1))
     for s in range(n):
         a, b = int(cu[s]), int(cu[s + 1])
-        seg = np.concatenate([np.zeros((W - 1, u.shape[1])), u[a:b]], axis=0)
+        hist = (np.zeros((W - 1, u.shape[1])) if initial_state is None else
+                np.asarray(initial_state[s], dtype=np.float64).T)
+        seg = np.concatenate([hist, u[a:b]], axis=0)
         acc = np.zeros((b - a, u.shape[1]))
         for j in range(W):
             acc += w[:, j][None, :] * seg[j:j + (b - a)]
@@ -264,7 +267,7 @@ def causal_conv_silu(u, conv_w, cu_seqlens):
 
 
 def frontend(x, w_in, conv_w, cu_seqlens, h_k, h_v, d, rms_eps=1e-6,
-             l2_eps=1e-6):
+             l2_eps=1e-6, conv_initial=None):
     """Pre-mixer RMSNorm, fused input projection, short conv + SiLU on q|k|v,
     per-head L2 norm of q and k, and the gates.
 
@@ -277,7 +280,8 @@ def frontend(x, w_in, conv_w, cu_seqlens, h_k, h_v, d, rms_eps=1e-6,
     p = xh @ W
     nq = h_k * d
     conv_dim = 2 * nq + h_v * d
-    c, conv_state = causal_conv_silu(p[:, :conv_dim], _f64(conv_w), cu_seqlens)
+    c, conv_state = causal_conv_silu(p[:, :conv_dim], _f64(conv_w), cu_seqlens,
+                                     conv_initial)
     T = x.shape[0]
     q = l2norm_rows(c[:, :nq].reshape(T, h_k, d), l2_eps)
     k = l2norm_rows(c[:, nq:2 * nq].reshape(T, h_k, d), l2_eps)
@@ -312,26 +316,47 @@ def replay_group(anchors, weights, cu_seqlens, layer_kind, h_k, h_v, d,
 
     Returns (states [n_gdn][N][h_v][d][d], conv_states [n_gdn][N][conv][W-1]).
     """
-    x = _f64(anchors)
+    out = extend_group(anchors, weights, cu_seqlens, layer_kind, h_k, h_v, d, rms_eps=rms_eps,
+                       l2_eps=l2_eps, want_hidden=False, return_trace=return_trace)
+    return (out[0], out[1], out[3]) if return_trace else (out[0], out[1])
+
+
+def extend_group(tokens, weights, cu_seqlens, layer_kind, h_k, h_v, d, initial_states=None,
+                 initial_conv_states=None, rms_eps=1e-6, l2_eps=1e-6, want_hidden=True,
+                 return_trace=False):
+    """Run new tokens through one group from given per-layer states and conv
+    windows ("Tail-Replay", section 3: the unmatched tokens continue from the
+    reconstructed states).  With no initial states this is the replay above;
+    with want_hidden the last layer also forms its mixer output and the
+    group's output hidden states are returned.
+
+    Returns (states, conv_states, hidden [T][hidden] or None, trace or None).
+    """
+    x = _f64(tokens)
     gdn_layers = [i for i, kind in enumerate(layer_kind) if kind == GDN]
     states, conv_states, trace = [], [], []
+    hidden = None
     for li, idx in enumerate(gdn_layers):
         w = weights[li]
         last = li == len(gdn_layers) - 1
-        fe = frontend(x, w.w_in, w.conv_w, cu_seqlens, h_k, h_v, d, rms_eps,
-                      l2_eps)
+        full = not last or want_hidden
+        fe = frontend(x, w.w_in, w.conv_w, cu_seqlens, h_k, h_v, d, rms_eps, l2_eps,
+                      None if initial_conv_states is None else initial_conv_states[li])
         S, o = gdn(fe["q"], fe["k"], fe["v"], fe["log_alpha"], fe["beta"],
                    cu_seqlens, h_k, h_v, alpha_is_log=True, erase=True,
-                   want_o=not last)
+                   initial_state=None if initial_states is None else initial_states[li],
+                   want_o=full)
         states.append(S)
         conv_states.append(fe["conv_state"])
         if return_trace:
             trace.append(dict(x=x, **fe, o=o))
-        if not last:
+        if full:
             x = x + output_path(o, fe["z"], w.w_out, rms_eps)
-    out = (np.stack(states) if states else np.zeros((0,)),
-           np.stack(conv_states) if conv_states else np.zeros((0,)))
-    return (out + (trace,)) if return_trace else out
+        if last and want_hidden:
+            hidden = x
+    st = np.stack(states) if states else np.zeros((0,))
+    cs = np.stack(conv_states) if conv_states else np.zeros((0,))
+    return st, cs, hidden, (trace if return_trace else None)
 
 
 def rel_fro(x, ref):

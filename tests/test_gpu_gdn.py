@@ -96,13 +96,15 @@ def test_value_head_pairs(d, hk, erase):
     np.testing.assert_array_equal(S, S2)
 
 
-@pytest.mark.parametrize("n_seqs,hk,hv", [(16, 32, 32), (12, 16, 32), (4, 16, 32)])
+@pytest.mark.parametrize("n_seqs,hk,hv", [(16, 32, 32), (12, 16, 32), (8, 16, 32),
+                                          (4, 16, 32)])
 @pytest.mark.parametrize("erase", [True, False])
 def test_launch_shapes(n_seqs, hk, hv, erase):
     """The launch picks its workgroup shape from the number of (sequence,
     value head) chains: 512 chains with one value head per key head and 384
-    chains take one head of 4 waves per workgroup, 128 chains one head of 8
-    waves (pairs of heads are covered above).  Full parity with ragged
+    chains take one head of 4 waves per workgroup, 256 chains one head of 8
+    waves, 128 chains two workgroups of 4 waves per chain (value columns
+    split; pairs of heads are covered above).  Full parity with ragged
     lengths and an initial state, and state-only equals the full run."""
     lens = (PAIR_LENS * 2)[:n_seqs]
     c = gdn_case(lens, hk, hv, 128, "bf16", seed=7 * n_seqs + hk + int(erase), normalize_q=True,
@@ -264,13 +266,14 @@ def test_full_size_every_sequence(which):
     assert ws <= 2 * TOL_BF16 and wo <= 2 * TOL_BF16
 
 
-@pytest.mark.parametrize("n_seqs", [16, 9])
+@pytest.mark.parametrize("n_seqs", [16, 9, 8])
 def test_packed_equals_solo_across_launch_shapes(n_seqs):
     """16 sequences x 32 value heads (512 chains: value-head pairs per
-    workgroup) and 9 x 32 (288 chains: one head of 4 waves) against each
-    sequence replayed alone (32 chains: one head of 8 waves): bit-identical
-    states and outputs, so no result depends on the launch shape or on a
-    sequence's neighbours."""
+    workgroup), 9 x 32 (288 chains: one head of 4 waves) and 8 x 32 (256
+    chains: one head of 8 waves) against each sequence replayed alone (32
+    chains: two workgroups of 4 waves per chain): bit-identical states and
+    outputs, so no result depends on the launch shape or on a sequence's
+    neighbours."""
     lens = (PAIR_LENS * 2)[:n_seqs]
     c = gdn_case(lens, 16, 32, 128, "bf16", seed=60 + n_seqs, normalize_q=True,
                  initial_state=True)

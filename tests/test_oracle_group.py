@@ -222,3 +222,59 @@ def test_bf16_rounding_is_rne():
     assert b[2] == 1.0 + 2 ** -6           # tie to even (up)
     assert b[3] == -2.5
     assert np.isfinite(b[4])
+
+
+# ---------------------------------------------------------------------------
+# continuation from a carried-in state ("Tail-Replay", section 3: the
+# unmatched tokens continue from the reconstructed states)
+# ---------------------------------------------------------------------------
+def test_causal_conv_with_history_against_numpy_convolve():
+    """With a carried-in window the conv is np.convolve over history +
+    sequence, and the returned window is the last W-1 rows of that."""
+    rng = np.random.default_rng(5)
+    W, C = 4, 3
+    lens = [5, 1, 0, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    u = rng.standard_normal((cu[-1], C))
+    w = rng.standard_normal((C, W))
+    hist = rng.standard_normal((len(lens), C, W - 1))
+    y, st = oracle.causal_conv_silu(u, w, cu, hist)
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        for c in range(C):
+            seq = np.concatenate([hist[s, c], u[a:b, c]])
+            # tap W-1 on the current sample; the history supplies the W-1
+            # samples before the sequence start
+            ref = np.convolve(seq, w[c, ::-1])[W - 1:W - 1 + (b - a)]
+            np.testing.assert_allclose(y[a:b, c], special.expit(ref) * ref, rtol=1e-12,
+                                       atol=1e-14)
+            np.testing.assert_allclose(st[s, c], seq[-(W - 1):], rtol=0, atol=0)
+
+
+def test_extend_group_equals_the_whole_run():
+    """Replaying a prefix and extending it by the rest from the carried
+    states and conv windows gives the states, windows and output hidden
+    states of one run over the whole sequence (the state and the window
+    summarise the prefix exactly)."""
+    g = _group([23, 9, 40], 21, 16, 2, 4, 4, [GDN, GDN, GDN])
+    cut = [10, 9, 1]
+    cu = g.cu_seqlens
+    pre_rows = np.concatenate([np.arange(cu[i], cu[i] + cut[i]) for i in range(3)])
+    tail_rows = np.concatenate([np.arange(cu[i] + cut[i], cu[i + 1]) for i in range(3)])
+    cu_pre = np.concatenate([[0], np.cumsum(cut)]).astype(np.int32)
+    tail_lens = [int(cu[i + 1] - cu[i]) - cut[i] for i in range(3)]
+    cu_tail = np.concatenate([[0], np.cumsum(tail_lens)]).astype(np.int32)
+    S_full, C_full, H_full, _ = oracle.extend_group(g.anchors, g.weights, cu, g.layer_kind,
+                                                    2, 4, 4)
+    S_pre, C_pre = oracle.replay_group(g.anchors[pre_rows], g.weights, cu_pre, g.layer_kind,
+                                       2, 4, 4)
+    S_ext, C_ext, H_ext, _ = oracle.extend_group(g.anchors[tail_rows], g.weights, cu_tail,
+                                                 g.layer_kind, 2, 4, 4, initial_states=S_pre,
+                                                 initial_conv_states=C_pre)
+    np.testing.assert_allclose(S_ext, S_full, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(C_ext, C_full, rtol=0, atol=0)
+    np.testing.assert_allclose(H_ext, H_full[tail_rows], rtol=1e-10, atol=1e-12)
+    # replay without the carried window (zero history) is a different result
+    S_bad, _, _, _ = oracle.extend_group(g.anchors[tail_rows], g.weights, cu_tail, g.layer_kind,
+                                         2, 4, 4, initial_states=S_pre)
+    assert oracle.rel_fro(S_bad, S_full) > 1e-6
