@@ -340,6 +340,105 @@ def bench_group(steps, warmup, to_dev):
     return out
 
 
+def bench_continuation_and_handoff(steps, warmup, to_dev):
+    """Single-token decode from reconstructed states (64 sequences x 32
+    heads, d = 128: each state read and written once), the sparse-anchor
+    gather from a pinned host-memory pool (over the host link) and its
+    overlap with a replay on another stream, and a small batch through the
+    group as an eager call against its bucketed HIP graph."""
+    import numpy as np
+    import torch
+    import linear_attention_state_anchor_amd as sr
+    from linear_attention_state_anchor_amd.graphs import GroupReplayGraphs
+    from replay_inputs import PAGE, config_c5, gdn_case
+
+    out = {}
+    # decode step
+    c = gdn_case([1] * 64, 16, 32, 128, "bf16", seed=7, normalize_q=True)
+    q, k, v, a, b = (to_dev(x) for x in (c.q, c.k, c.v, c.alpha, c.beta))
+    S = torch.randn((64, 32, 128, 128), dtype=torch.float32, device="cuda:0") * 0.1
+    o = torch.empty((64, 32, 128), dtype=torch.bfloat16, device="cuda:0")
+    t = time_steps(lambda: sr.gdn_decode_step(q, k, v, a, b, S, alpha_is_log=True, o=o),
+                   steps, warmup)
+    byts = 2 * S.numel() * 4 + 64 * (2 * 16 + 2 * 32) * 128 * 2 + 64 * 32 * 8
+    out["decode_step"] = {
+        "workload": "one decode token for 64 sequences from their states, 16 key / 32 value "
+                    "heads, d=128, fp32 state in place, bf16 in/out",
+        "ms_per_step": t["mean_ms"], "median_ms": t["median_ms"],
+        "tokens_per_s": 64 / (t["mean_ms"] / 1e3),
+        "hbm_gbs": byts / (t["mean_ms"] / 1e3) / 1e9,
+        "hbm_frac": byts / (t["mean_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": byts}
+    del S
+    # sparse anchors kept in pinned host memory, gathered over the host link
+    pc, wts = config_c5()
+    offs = sr.DENSE_NEAR_BOUNDARY_1_16
+    m = [int(x) for x in pc.matched_len]
+    n_anchor = [len(offs) * (x // PAGE) + sum(o_ < x % PAGE for o_ in offs) for x in m]
+    k_sp = sr.replay_budget(n_anchor, 0.05, 512)
+    Ts = sum(k_sp)
+    hpool = torch.empty((pc.n_pages, len(offs), 2560), dtype=torch.bfloat16).pin_memory()
+    hpool.view(torch.int16).random_(-16000, 16000)
+    pt, ml = to_dev(pc.page_table), to_dev(pc.matched_len)
+    ksp = to_dev(np.asarray(k_sp, np.int32))
+    sp = torch.empty((Ts, 2560), dtype=torch.bfloat16, device="cuda:0")
+    cus = torch.empty((65,), dtype=torch.int32, device="cuda:0")
+    hg = lambda: sr.gather_anchors(hpool, offs, pt, ml, ksp, Ts, packed=sp, cu_seqlens=cus,
+                                   positions=False)
+    tg = time_steps(hg, steps, warmup)
+    # overlap: the host gather on a copy stream next to a replay on this one
+    packed5 = [sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), 16, 32, 128)
+               for w in wts]
+    anchors_prev = torch.randn((Ts, 2560), device="cuda:0").to(torch.bfloat16)
+    cu_prev = cus.clone()
+    hg()
+    torch.cuda.synchronize()
+    cu_prev.copy_(cus)
+    st = torch.empty((3, 64, 32, 128, 128), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty((sr.group_workspace_bytes(Ts, 2560, 16, 32, 128, n_seqs=64),),
+                     dtype=torch.uint8, device="cuda:0")
+    replay = lambda: sr.replay_group(anchors_prev, packed5, cu_prev, [0, 0, 0, 1], 16, 32, 128,
+                                     states=st, workspace=ws)
+    tr = time_steps(replay, max(3, steps // 4), 2)
+    copy_stream = torch.cuda.Stream()
+
+    def both():
+        copy_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(copy_stream):
+            hg()
+        replay()
+        torch.cuda.current_stream().wait_stream(copy_stream)
+    tb = time_steps(both, max(3, steps // 4), 2)
+    gb = Ts * 2560 * 2 / 1e9
+    out["host_pool_gather"] = {
+        "workload": f"sparse anchors (1/16, next to the page boundary) of the 64 varlen hits in "
+                    f"pinned host memory, k = min(ceil(0.05 n), 512) (T = {Ts}), gathered over "
+                    f"the host link; next to a 3-layer group replay of a previous batch on "
+                    f"another stream",
+        "gather_ms": tg["mean_ms"], "host_link_gbs": gb / (tg["mean_ms"] / 1e3),
+        "replay_ms": tr["mean_ms"], "gather_and_replay_overlapped_ms": tb["mean_ms"],
+        "serial_sum_ms": tg["mean_ms"] + tr["mean_ms"]}
+    del hpool, ws, st
+    # a small batch: eager group call against its bucketed graph
+    g4 = [sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), 16, 32, 128)
+          for w in wts]
+    small = torch.randn((4 * 128, 2560), device="cuda:0").to(torch.bfloat16)
+    cu4 = to_dev(np.arange(0, 513, 128, dtype=np.int32))
+    graphs = GroupReplayGraphs(g4, [0, 0, 0, 1], 16, 32, 128, 2560, buckets=(512,),
+                               max_requests=4)
+    st4 = torch.empty((3, 4, 32, 128, 128), dtype=torch.float32, device="cuda:0")
+    ws4 = torch.empty((sr.group_workspace_bytes(512, 2560, 16, 32, 128, n_seqs=4),),
+                      dtype=torch.uint8, device="cuda:0")
+    te = time_steps(lambda: sr.replay_group(small, g4, cu4, [0, 0, 0, 1], 16, 32, 128,
+                                            states=st4, workspace=ws4), steps, warmup)
+    graphs.run(small, cu4)
+    tgr = time_steps(lambda: graphs.run(small, cu4), steps, warmup)
+    out["graph_bucket"] = {
+        "workload": "4 requests x 128 anchors through the 3-layer hidden-2560 group: eager "
+                    "library call against the graph of its 512-token bucket",
+        "eager_ms": te["mean_ms"], "graph_ms": tgr["mean_ms"]}
+    return out
+
+
 def error_vs_k(to_dev, n_req=8, ks=(16, 32, 64, 128, 256, 512)):
     """Replay error against the replay length (untimed report).
 
@@ -483,6 +582,7 @@ def main():
                                       cu, S))
     if not args.no_group:
         line.update(bench_group(min(20, max(3, args.steps // 5)), 3, to_dev))
+        line.update(bench_continuation_and_handoff(min(50, args.steps), 5, to_dev))
     if not args.no_cpu_baseline:
         # the benchmarked launch's S and o, against the oracle
         step()

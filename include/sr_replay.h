@@ -184,7 +184,13 @@ int sr_check_replay_inputs(const sr_gdn_desc* desc, const sr_gdn_io* io, void* s
  *               untouched)
  *   cu_seqlens_out [n_req+1] int32
  * hidden * elem_bytes must be a multiple of 16.  The host-side total keeps
- * the launch free of a device-to-host read.  Out-of-range page ids and
+ * the launch free of a device-to-host read.  The pool may also live in
+ * pinned host memory (hipHostMalloc; "SuffixReplay", System Design, Anchor
+ * Sidecar: anchors can stay in host DRAM while KV pages stay in HBM): the
+ * kernel then reads the anchor rows over the host link and writes the packed
+ * rows to device memory, so a gather issued on its own stream overlaps work
+ * on others.  A host pool that is not pinned and device-mapped is rejected
+ * with SR_EINVAL.  Out-of-range page ids and
  * page-table columns are clamped (the launch stays in bounds; the copied
  * rows are then meaningless): sr_check_gather_inputs reports them.
  * ------------------------------------------------------------------------ */
@@ -295,6 +301,13 @@ typedef struct {
   int32_t hidden, h_k, h_v, d, conv_width;
   float rms_eps, l2_eps;
   int32_t n_seqs, total_tokens, max_seqlen;
+  /* Layer-wise handoff ("SuffixReplay", System Design, Pipelined Replay
+   * Path: a consumer waits only for the layer whose state it reads): host
+   * array [n_gdn] of hipEvent_t (as void*), or NULL.  Entry l, if not NULL,
+   * is recorded on the stream right after GDN layer l's state (and conv
+   * window) is written, so another stream can hipStreamWaitEvent on it
+   * instead of on the whole group. */
+  void* const* layer_events;
 } sr_group_desc;
 
 /* Packed weights of one GDN layer, produced by sr_pack_gdn_layer into a

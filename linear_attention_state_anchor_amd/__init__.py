@@ -181,8 +181,17 @@ def check_replay_inputs(q, k, v, alpha, beta=None, cu_seqlens=None, initial_stat
 
 
 def _gather_common(pool, page_table, matched_len, suffix_len, rows):
-    _need(pool, "pool", ndim=3)
-    dev = pool.device
+    # the pool may sit in pinned host memory (read by the kernel over the
+    # host link); everything else is device memory
+    _need(page_table, "page_table", torch.int32, ndim=2)
+    dev = page_table.device
+    if pool.is_cuda:
+        _need(pool, "pool", ndim=3, device=dev)
+    else:
+        if not isinstance(pool, torch.Tensor) or not pool.is_pinned():
+            raise ValueError("a host pool must be a pinned (page-locked) tensor")
+        if not pool.is_contiguous() or pool.dim() != 3:
+            raise ValueError("pool must be a contiguous [P, rows, hidden] tensor")
     if pool.element_size() not in (2, 4):
         raise ValueError("pool elements must be 2 or 4 bytes")
     if pool.shape[1] != rows:
@@ -190,7 +199,6 @@ def _gather_common(pool, page_table, matched_len, suffix_len, rows):
     _need(matched_len, "matched_len", torch.int32, ndim=1, device=dev)
     n = matched_len.shape[0]
     _need(suffix_len, "suffix_len", torch.int32, (n,), device=dev)
-    _need(page_table, "page_table", torch.int32, ndim=2, device=dev)
     if page_table.shape[0] != n or page_table.shape[1] < 1:
         raise ValueError(f"page_table must be [{n}, max_pages >= 1], got "
                          f"{tuple(page_table.shape)}")
@@ -330,12 +338,29 @@ def pack_gdn_layer(w_in, conv_w, w_out, h_k, h_v, d):
     return out
 
 
-def _group_desc(kinds, hidden, h_k, h_v, d, conv_width, rms_eps, l2_eps, n, T, max_seqlen):
+def _event_handle(ev):
+    """Raw hipEvent_t of a torch.cuda.Event (created on first use)."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record()   # torch creates the event lazily, at its first record
+    return ctypes.c_void_p(ev.cuda_event)
+
+
+def _group_desc(kinds, hidden, h_k, h_v, d, conv_width, rms_eps, l2_eps, n, T, max_seqlen,
+                layer_events=None):
     kind_arr = (ctypes.c_int32 * max(len(kinds), 1))(*kinds)
+    ev_arr = None
+    if layer_events is not None:
+        n_gdn = sum(1 for x in kinds if x == SR_LAYER_GDN)
+        if len(layer_events) != n_gdn:
+            raise ValueError("one event (or None) per GDN layer")
+        ev_arr = (ctypes.c_void_p * max(n_gdn, 1))(*[_event_handle(e) for e in layer_events])
     desc = _lib.GroupDesc(len(kinds), ctypes.cast(kind_arr, ctypes.POINTER(ctypes.c_int32)),
                           hidden, h_k, h_v, d, conv_width, float(rms_eps), float(l2_eps),
-                          n, T, int(max_seqlen))
-    return desc, kind_arr
+                          n, T, int(max_seqlen),
+                          ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr else None)
+    return desc, (kind_arr, ev_arr)
 
 
 def group_workspace_bytes(total_tokens, hidden, h_k, h_v, d, conv_width=4, n_seqs=1,
@@ -348,7 +373,8 @@ def group_workspace_bytes(total_tokens, hidden, h_k, h_v, d, conv_width=4, n_seq
 
 
 def _group_prepare(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width,
-                   rms_eps, l2_eps, max_seqlen, want_conv_state, states, conv_states):
+                   rms_eps, l2_eps, max_seqlen, want_conv_state, states, conv_states,
+                   layer_events=None):
     _need(anchors, "anchors", torch.bfloat16, ndim=2)
     dev = anchors.device
     _need(cu_seqlens, "cu_seqlens", torch.int32, ndim=1, device=dev)
@@ -371,7 +397,7 @@ def _group_prepare(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d,
     if max_seqlen is None:
         max_seqlen = T
     desc, keep = _group_desc(kinds, hidden, h_k, h_v, d, conv_width, rms_eps, l2_eps, n, T,
-                             max_seqlen)
+                             max_seqlen, layer_events)
     if states is None:
         states = torch.empty((n_gdn, n, h_v, d, d), dtype=torch.float32, device=dev)
     else:
@@ -391,13 +417,16 @@ def _group_prepare(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d,
 
 def replay_group(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
                  conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None,
-                 want_conv_state=False, states=None, conv_states=None, workspace=None):
+                 want_conv_state=False, states=None, conv_states=None, workspace=None,
+                 layer_events=None):
     """Replay one group of linear-attention layers from its anchors
     (sr_replay_group).  Returns states fp32 [n_gdn, N, h_v, d, d] (and conv
-    states fp32 [n_gdn, N, conv_dim, width-1] if asked)."""
+    states fp32 [n_gdn, N, conv_dim, width-1] if asked).  layer_events: one
+    torch.cuda.Event (or None) per GDN layer, recorded as soon as that
+    layer's state is written (layer-wise handoff)."""
     desc, _keep, wts, states, conv, n_gdn, T = _group_prepare(
         anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width, rms_eps,
-        l2_eps, max_seqlen, want_conv_state, states, conv_states)
+        l2_eps, max_seqlen, want_conv_state, states, conv_states, layer_events)
     lib = _lib.load()
     ws_bytes = int(lib.sr_replay_group_workspace_bytes(ctypes.byref(desc)))
     if ws_bytes == 0 and n_gdn and T > 0:
@@ -422,14 +451,15 @@ def noalloc_max_bytes() -> int:
 
 def replay_group_noalloc(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
                          conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None,
-                         want_conv_state=False, states=None, conv_states=None):
+                         want_conv_state=False, states=None, conv_states=None,
+                         layer_events=None):
     """replay_group without a workspace allocation (sr_replay_group_noalloc):
     the library's static per-GPU workspace is used.  Pass preallocated
     `states` (and `conv_states`) to keep the call free of allocations.
     Calls that overlap on one GPU race."""
     desc, _keep, wts, states, conv, n_gdn, T = _group_prepare(
         anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width, rms_eps,
-        l2_eps, max_seqlen, want_conv_state, states, conv_states)
+        l2_eps, max_seqlen, want_conv_state, states, conv_states, layer_events)
     st = _lib.load().sr_replay_group_noalloc(ctypes.byref(desc), wts, _ptr(anchors),
                                              _ptr(cu_seqlens), _ptr(states), _ptr(conv),
                                              _stream())
@@ -440,13 +470,13 @@ def replay_group_noalloc(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h
 def extend_group(tokens, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
                  initial_states=None, initial_conv_states=None, want_hidden=True,
                  conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None, states=None,
-                 conv_states=None, workspace=None):
+                 conv_states=None, workspace=None, layer_events=None):
     """Continue a group from given per-layer states and conv windows over new
     tokens (sr_extend_group).  Returns (states, conv_states, hidden_out fp32
     [T, hidden] or None)."""
     desc, _keep, wts, states, conv, n_gdn, T = _group_prepare(
         tokens, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width, rms_eps,
-        l2_eps, max_seqlen, True, states, conv_states)
+        l2_eps, max_seqlen, True, states, conv_states, layer_events)
     dev = tokens.device
     n = cu_seqlens.shape[0] - 1
     if initial_states is not None:

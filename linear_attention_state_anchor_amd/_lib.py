@@ -41,7 +41,8 @@ class GroupDesc(ctypes.Structure):
                 ("hidden", c_i32), ("h_k", c_i32), ("h_v", c_i32), ("d", c_i32),
                 ("conv_width", c_i32), ("rms_eps", ctypes.c_float),
                 ("l2_eps", ctypes.c_float), ("n_seqs", c_i32),
-                ("total_tokens", c_i32), ("max_seqlen", c_i32)]
+                ("total_tokens", c_i32), ("max_seqlen", c_i32),
+                ("layer_events", ctypes.POINTER(c_p))]
 
 
 class LayerWeights(ctypes.Structure):

@@ -133,6 +133,21 @@ int gather(const void* pool, int32_t hidden, int32_t elem_bytes, int64_t n_block
     return n_req == 0 ? SR_ESHAPE : SR_EINVAL;
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (total_tokens > 0 && (!al16(pool) || !al16(packed))) return SR_EINVAL;
+  // A pool in pinned host memory is read through its device mapping; memory
+  // the runtime does not know (pageable host memory) is rejected.
+  const void* dev_pool = pool;
+  if (total_tokens > 0) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, pool) != hipSuccess) {
+      (void)hipGetLastError();
+      return SR_EINVAL;
+    }
+    if (attr.type == hipMemoryTypeUnregistered) return SR_EINVAL;
+    if (attr.type == hipMemoryTypeHost) {
+      if (!attr.devicePointer || !al16(attr.devicePointer)) return SR_EINVAL;
+      dev_pool = attr.devicePointer;
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_checks_enabled()) {
     const int c = check_gather(n_blocks, lay.a, lay.off, page_table, pt_stride, matched_len,
@@ -145,7 +160,7 @@ int gather(const void* pool, int32_t hidden, int32_t elem_bytes, int64_t n_block
   if (total_tokens > 0) {
     const int blocks = (total_tokens + 3) / 4;
     hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(pool), n_blocks, static_cast<int>(row_bytes),
+                       static_cast<const uint8_t*>(dev_pool), n_blocks, static_cast<int>(row_bytes),
                        lay, page_table, pt_stride, matched_len, suffix_len, n_req,
                        cu_seqlens_out, total_tokens, static_cast<uint8_t*>(packed),
                        positions_out);

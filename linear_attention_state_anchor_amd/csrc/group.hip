@@ -820,6 +820,11 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
     g.s_out = st;
     g.o = full ? ob : nullptr;
     if (sr::launch_gdn_chunk(g, s) != hipSuccess) return SR_ELAUNCH;
+    // layer-wise handoff: this layer's state and conv window are final now
+    if (d->layer_events && d->layer_events[li]) {
+      if (hipEventRecord(static_cast<hipEvent_t>(d->layer_events[li]), s) != hipSuccess)
+        return SR_ELAUNCH;
+    }
     if (!full || T == 0) continue;
     const int rows = T * d->h_v;
     const dim3 ngrid((rows + 15) / 16);
