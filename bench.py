@@ -418,24 +418,27 @@ def bench_continuation_and_handoff(steps, warmup, to_dev):
         "replay_ms": tr["mean_ms"], "gather_and_replay_overlapped_ms": tb["mean_ms"],
         "serial_sum_ms": tg["mean_ms"] + tr["mean_ms"]}
     del hpool, ws, st
-    # a small batch: eager group call against its bucketed graph
+    # small batches, where launching about two dozen kernels one by one
+    # costs host time: eager library call against the graph of its bucket
     g4 = [sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), 16, 32, 128)
           for w in wts]
-    small = torch.randn((4 * 128, 2560), device="cuda:0").to(torch.bfloat16)
-    cu4 = to_dev(np.arange(0, 513, 128, dtype=np.int32))
-    graphs = GroupReplayGraphs(g4, [0, 0, 0, 1], 16, 32, 128, 2560, buckets=(512,),
+    graphs = GroupReplayGraphs(g4, [0, 0, 0, 1], 16, 32, 128, 2560, buckets=(64, 512),
                                max_requests=4)
-    st4 = torch.empty((3, 4, 32, 128, 128), dtype=torch.float32, device="cuda:0")
-    ws4 = torch.empty((sr.group_workspace_bytes(512, 2560, 16, 32, 128, n_seqs=4),),
-                      dtype=torch.uint8, device="cuda:0")
-    te = time_steps(lambda: sr.replay_group(small, g4, cu4, [0, 0, 0, 1], 16, 32, 128,
-                                            states=st4, workspace=ws4), steps, warmup)
-    graphs.run(small, cu4)
-    tgr = time_steps(lambda: graphs.run(small, cu4), steps, warmup)
-    out["graph_bucket"] = {
-        "workload": "4 requests x 128 anchors through the 3-layer hidden-2560 group: eager "
-                    "library call against the graph of its 512-token bucket",
-        "eager_ms": te["mean_ms"], "graph_ms": tgr["mean_ms"]}
+    for n_tok in (64, 512):
+        small = torch.randn((n_tok, 2560), device="cuda:0").to(torch.bfloat16)
+        cu4 = to_dev(np.arange(0, n_tok + 1, n_tok // 4, dtype=np.int32))
+        st4 = torch.empty((3, 4, 32, 128, 128), dtype=torch.float32, device="cuda:0")
+        ws4 = torch.empty((sr.group_workspace_bytes(n_tok, 2560, 16, 32, 128, n_seqs=4),),
+                          dtype=torch.uint8, device="cuda:0")
+        te = time_steps(lambda: sr.replay_group(small, g4, cu4, [0, 0, 0, 1], 16, 32, 128,
+                                                states=st4, workspace=ws4), steps, warmup)
+        graphs.run(small, cu4)
+        tgr = time_steps(lambda: graphs.run(small, cu4), steps, warmup)
+        out[f"graph_bucket_{n_tok}"] = {
+            "workload": f"4 requests x {n_tok // 4} anchors through the 3-layer hidden-2560 "
+                        f"group: eager library call against run() of its {n_tok}-token bucket "
+                        f"graph (input copies included)",
+            "eager_ms": te["mean_ms"], "graph_ms": tgr["mean_ms"]}
     return out
 
 

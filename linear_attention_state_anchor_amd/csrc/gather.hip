@@ -20,6 +20,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "sr_common.hpp"
 #include "sr_internal.hpp"
 
@@ -74,14 +76,37 @@ __global__ __launch_bounds__(1024) void suffix_cu_kernel(const int32_t* __restri
   }
 }
 
+__device__ __forceinline__ void copy_row(int r, int lane, const uint8_t* __restrict__ pool,
+                                         int64_t n_blocks, int row_bytes, const AnchorLayout& lay,
+                                         const int32_t* __restrict__ pt, int pt_stride,
+                                         const int32_t* __restrict__ m_len,
+                                         const int32_t* __restrict__ k_len, int n_req,
+                                         const int32_t* __restrict__ cu, uint8_t* __restrict__ out,
+                                         int32_t* __restrict__ positions);
+
+// One wave per packed row, grid-stride over the rows (the launch bounds the
+// grid: a gather from host memory is bound by the host link and only needs
+// a few CUs, which leaves the rest to work on other streams).
 __global__ __launch_bounds__(256) void gather_rows_kernel(
     const uint8_t* __restrict__ pool, int64_t n_blocks, int row_bytes, AnchorLayout lay,
     const int32_t* __restrict__ pt, int pt_stride, const int32_t* __restrict__ m_len,
     const int32_t* __restrict__ k_len, int n_req, const int32_t* __restrict__ cu,
     int total, uint8_t* __restrict__ out, int32_t* __restrict__ positions) {
-  const int r = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  if (r >= total || r >= cu[n_req]) return;  // rows past sum(k) stay untouched
+  const int rows = min(total, cu[n_req]);  // rows past sum(k) stay untouched
+  for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < rows; r += gridDim.x * 4)
+    copy_row(r, lane, pool, n_blocks, row_bytes, lay, pt, pt_stride, m_len, k_len, n_req, cu,
+             out, positions);
+}
+
+// Packed row r (one wave): find its request, anchor, block and row, copy it.
+__device__ __forceinline__ void copy_row(int r, int lane, const uint8_t* __restrict__ pool,
+                                         int64_t n_blocks, int row_bytes, const AnchorLayout& lay,
+                                         const int32_t* __restrict__ pt, int pt_stride,
+                                         const int32_t* __restrict__ m_len,
+                                         const int32_t* __restrict__ k_len, int n_req,
+                                         const int32_t* __restrict__ cu, uint8_t* __restrict__ out,
+                                         int32_t* __restrict__ positions) {
   // request owning row r: largest i with cu[i] <= r
   int lo = 0, hi = n_req - 1;
   while (lo < hi) {
@@ -136,6 +161,7 @@ int gather(const void* pool, int32_t hidden, int32_t elem_bytes, int64_t n_block
   // A pool in pinned host memory is read through its device mapping; memory
   // the runtime does not know (pageable host memory) is rejected.
   const void* dev_pool = pool;
+  bool dev_host = false;  // the pool is host memory read through a mapping
   if (total_tokens > 0) {
     hipPointerAttribute_t attr{};
     if (hipPointerGetAttributes(&attr, pool) != hipSuccess) {
@@ -146,6 +172,7 @@ int gather(const void* pool, int32_t hidden, int32_t elem_bytes, int64_t n_block
     if (attr.type == hipMemoryTypeHost) {
       if (!attr.devicePointer || !al16(attr.devicePointer)) return SR_EINVAL;
       dev_pool = attr.devicePointer;
+      dev_host = true;
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -158,7 +185,9 @@ int gather(const void* pool, int32_t hidden, int32_t elem_bytes, int64_t n_block
                      cu_seqlens_out);
   if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
   if (total_tokens > 0) {
-    const int blocks = (total_tokens + 3) / 4;
+    // device pool: enough workgroups to fill the chip; host pool: a few
+    const int cap = dev_host ? 64 : 4096;
+    const int blocks = std::min((total_tokens + 3) / 4, cap);
     hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, s,
                        static_cast<const uint8_t*>(dev_pool), n_blocks, static_cast<int>(row_bytes),
                        lay, page_table, pt_stride, matched_len, suffix_len, n_req,
