@@ -268,6 +268,30 @@ def bench_group(steps, warmup, to_dev):
         "tflops": fl / (ms / 1e3) / 1e12, "mfma_frac": fl / (ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFS,
     }
     del ws
+    # the same group with an FFN block after each intermediate layer
+    from replay_inputs import FFN_DIM
+    gf = config_c4(ffn_dim=FFN_DIM)
+    packed_f = [(sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), 16, 32,
+                                   128),
+                 sr.pack_ffn(to_dev(w.w_gate), to_dev(w.w_up), to_dev(w.w_down)))
+                for w in gf.weights]
+    wsf = torch.empty((sr.group_workspace_bytes(T, 2560, 16, 32, 128, n_seqs=g.n_seqs,
+                                                layer_kind=g.layer_kind, ffn_dim=FFN_DIM),),
+                      dtype=torch.uint8, device="cuda:0")
+    af = to_dev(gf.anchors)
+    t = time_steps(lambda: sr.replay_group(af, packed_f, cu, g.layer_kind, 16, 32, 128,
+                                           states=states, workspace=wsf, ffn_dim=FFN_DIM),
+                   steps, warmup)
+    flf = fl + 2 * 3 * 2.0 * T * 2560 * FFN_DIM
+    ms = t["mean_ms"]
+    out["group_ffn"] = {
+        "workload": f"the 4 x 1638 group with a SwiGLU FFN (width {FFN_DIM}) after the two "
+                    f"intermediate GDN layers (the last layer's FFN is skipped)",
+        "ms_per_step": ms, "median_ms": t["median_ms"],
+        "replayed_tokens_per_s_per_layer": 3 * T / (ms / 1e3),
+        "tflops": flf / (ms / 1e3) / 1e12, "mfma_frac": flf / (ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFS,
+    }
+    del wsf, packed_f
     # varlen: gather + group
     pc, wts = config_c5()
     packed5 = [sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), 16, 32, 128)

@@ -308,12 +308,21 @@ typedef struct {
    * window) is written, so another stream can hipStreamWaitEvent on it
    * instead of on the whole group. */
   void* const* layer_events;
+  /* FFN width of the layers' feed-forward blocks (0: no FFN), a multiple of
+   * 64.  A layer whose weights carry an FFN (sr_gdn_layer_weights.ffn) runs
+   * x <- x + W_down (SiLU(RMSNorm(x) W_gate) * (RMSNorm(x) W_up)) after its
+   * mixer ("Tail-Replay", section 3: replay omits the group's final FFN:
+   * the last layer's FFN runs only when the group's output hidden states
+   * are asked for, sr_extend_group). */
+  int32_t ffn_dim;
 } sr_group_desc;
 
 /* Packed weights of one GDN layer, produced by sr_pack_gdn_layer into a
  * caller-owned buffer of sr_packed_layer_bytes() bytes. */
 typedef struct {
-  const void* packed; /* device, 256-aligned */
+  const void* packed; /* device, 256-aligned: sr_pack_gdn_layer output        */
+  const void* ffn;    /* device, 256-aligned: sr_pack_ffn output, or NULL (no
+                         FFN block after this layer)                          */
 } sr_gdn_layer_weights;
 
 /* Size in bytes of one packed layer for these shapes. */
@@ -328,6 +337,15 @@ size_t sr_packed_layer_bytes(int32_t hidden, int32_t h_k, int32_t h_v,
 int sr_pack_gdn_layer(const void* w_in, const void* conv_w, const void* w_out,
                       int32_t hidden, int32_t h_k, int32_t h_v, int32_t d,
                       int32_t conv_width, void* packed, void* stream);
+
+/* FFN block of one layer: w_gate, w_up bf16 [hidden][ffn_dim], w_down bf16
+ * [ffn_dim][hidden] -> packed (device, sr_packed_ffn_bytes bytes): fp16,
+ * k-contiguous, gate and up columns interleaved in pairs so the gate|up
+ * product and SiLU(g) * u come out of one matrix-core pass.  hidden % 128
+ * == 0, ffn_dim % 64 == 0. */
+size_t sr_packed_ffn_bytes(int32_t hidden, int32_t ffn_dim);
+int sr_pack_ffn(const void* w_gate, const void* w_up, const void* w_down, int32_t hidden,
+                int32_t ffn_dim, void* packed, void* stream);
 
 size_t sr_replay_group_workspace_bytes(const sr_group_desc* desc);
 

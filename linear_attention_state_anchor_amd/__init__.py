@@ -26,7 +26,8 @@ from ._lib import (ReplayArgumentError, ReplayError, SR_BF16, SR_F16, SR_F32, SR
 __all__ = ["gdn_replay_state", "gdn_decode_step", "extend_group", "check_replay_inputs",
            "gather_suffix", "gather_anchors",
            "check_gather_inputs", "replay_budget", "pack_gdn_layer", "replay_group",
-           "packed_layer_bytes", "group_workspace_bytes", "replay_group_noalloc",
+           "packed_layer_bytes", "pack_ffn", "packed_ffn_bytes", "group_workspace_bytes",
+           "replay_group_noalloc",
            "noalloc_max_bytes", "version", "ReplayError",
            "ReplayArgumentError", "SR_LAYER_GDN", "SR_LAYER_FA", "PAGE",
            "DENSE_NEAR_BOUNDARY_1_16", "UNIFORM_1_16"]
@@ -306,6 +307,27 @@ def replay_budget(n_anchors, ratio=0.05, k_max=0):
     return [int(out[i]) for i in range(len(ns))]
 
 
+def packed_ffn_bytes(hidden, ffn_dim) -> int:
+    return int(_lib.load().sr_packed_ffn_bytes(hidden, ffn_dim))
+
+
+def pack_ffn(w_gate, w_up, w_down):
+    """Pack one FFN block's bf16 weights (sr_pack_ffn): w_gate, w_up [hidden,
+    F], w_down [F, hidden].  Returns a uint8 device tensor."""
+    _need(w_gate, "w_gate", torch.bfloat16, ndim=2)
+    hidden, F = w_gate.shape
+    _need(w_up, "w_up", torch.bfloat16, (hidden, F), device=w_gate.device)
+    _need(w_down, "w_down", torch.bfloat16, (F, hidden), device=w_gate.device)
+    nbytes = packed_ffn_bytes(hidden, F)
+    if nbytes == 0:
+        raise ValueError("unsupported FFN shape")
+    out = torch.empty((nbytes,), dtype=torch.uint8, device=w_gate.device)
+    st = _lib.load().sr_pack_ffn(_ptr(w_gate), _ptr(w_up), _ptr(w_down), hidden, F, _ptr(out),
+                                 _stream())
+    _lib.check("sr_pack_ffn", st)
+    return out
+
+
 def packed_layer_bytes(hidden, h_k, h_v, d, conv_width=4) -> int:
     return int(_lib.load().sr_packed_layer_bytes(hidden, h_k, h_v, d, conv_width))
 
@@ -348,7 +370,7 @@ def _event_handle(ev):
 
 
 def _group_desc(kinds, hidden, h_k, h_v, d, conv_width, rms_eps, l2_eps, n, T, max_seqlen,
-                layer_events=None):
+                layer_events=None, ffn_dim=0):
     kind_arr = (ctypes.c_int32 * max(len(kinds), 1))(*kinds)
     ev_arr = None
     if layer_events is not None:
@@ -359,22 +381,23 @@ def _group_desc(kinds, hidden, h_k, h_v, d, conv_width, rms_eps, l2_eps, n, T, m
     desc = _lib.GroupDesc(len(kinds), ctypes.cast(kind_arr, ctypes.POINTER(ctypes.c_int32)),
                           hidden, h_k, h_v, d, conv_width, float(rms_eps), float(l2_eps),
                           n, T, int(max_seqlen),
-                          ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr else None)
+                          ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p)) if ev_arr else None,
+                          int(ffn_dim))
     return desc, (kind_arr, ev_arr)
 
 
 def group_workspace_bytes(total_tokens, hidden, h_k, h_v, d, conv_width=4, n_seqs=1,
-                          layer_kind=(SR_LAYER_GDN,)) -> int:
+                          layer_kind=(SR_LAYER_GDN,), ffn_dim=0) -> int:
     """Workspace bytes of one replay_group call (sr_replay_group_workspace_bytes)."""
     kinds = [int(x) for x in layer_kind]
     desc, _keep = _group_desc(kinds, hidden, h_k, h_v, d, conv_width, 1e-6, 1e-6, n_seqs,
-                              total_tokens, total_tokens)
+                              total_tokens, total_tokens, None, ffn_dim)
     return int(_lib.load().sr_replay_group_workspace_bytes(ctypes.byref(desc)))
 
 
 def _group_prepare(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width,
                    rms_eps, l2_eps, max_seqlen, want_conv_state, states, conv_states,
-                   layer_events=None):
+                   layer_events=None, ffn_dim=0):
     _need(anchors, "anchors", torch.bfloat16, ndim=2)
     dev = anchors.device
     _need(cu_seqlens, "cu_seqlens", torch.int32, ndim=1, device=dev)
@@ -389,15 +412,26 @@ def _group_prepare(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d,
     need_bytes = packed_layer_bytes(hidden, h_k, h_v, d, conv_width)
     if n_gdn and need_bytes == 0:
         raise ValueError("unsupported layer shape")
+    ffn_bytes = packed_ffn_bytes(hidden, ffn_dim) if ffn_dim else 0
+    pairs = []
     for i, w in enumerate(packed_weights):
-        _need(w, f"packed_weights[{i}]", torch.uint8, ndim=1, device=dev)
-        if w.numel() < need_bytes:
-            raise ValueError(f"packed_weights[{i}] holds {w.numel()} bytes, the layer shape "
+        w_mix, w_ffn = (w if isinstance(w, (tuple, list)) else (w, None))
+        _need(w_mix, f"packed_weights[{i}]", torch.uint8, ndim=1, device=dev)
+        if w_mix.numel() < need_bytes:
+            raise ValueError(f"packed_weights[{i}] holds {w_mix.numel()} bytes, the layer shape "
                              f"needs {need_bytes} (packed for another shape?)")
+        if w_ffn is not None:
+            if not ffn_dim:
+                raise ValueError("FFN weights given but ffn_dim is 0")
+            _need(w_ffn, f"packed FFN weights [{i}]", torch.uint8, ndim=1, device=dev)
+            if w_ffn.numel() < ffn_bytes:
+                raise ValueError(f"packed FFN weights [{i}] hold {w_ffn.numel()} bytes, "
+                                 f"ffn_dim {ffn_dim} needs {ffn_bytes}")
+        pairs.append((w_mix, w_ffn))
     if max_seqlen is None:
         max_seqlen = T
     desc, keep = _group_desc(kinds, hidden, h_k, h_v, d, conv_width, rms_eps, l2_eps, n, T,
-                             max_seqlen, layer_events)
+                             max_seqlen, layer_events, ffn_dim)
     if states is None:
         states = torch.empty((n_gdn, n, h_v, d, d), dtype=torch.float32, device=dev)
     else:
@@ -411,22 +445,25 @@ def _group_prepare(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d,
         else:
             _need(conv_states, "conv_states", torch.float32, shape, device=dev)
             conv = conv_states
-    wts = (_lib.LayerWeights * max(n_gdn, 1))(*[_lib.LayerWeights(_ptr(w)) for w in packed_weights])
+    wts = (_lib.LayerWeights * max(n_gdn, 1))(*[_lib.LayerWeights(_ptr(a), _ptr(b))
+                                                 for a, b in pairs])
     return desc, keep, wts, states, conv, n_gdn, T
 
 
 def replay_group(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
                  conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None,
                  want_conv_state=False, states=None, conv_states=None, workspace=None,
-                 layer_events=None):
+                 layer_events=None, ffn_dim=0):
     """Replay one group of linear-attention layers from its anchors
     (sr_replay_group).  Returns states fp32 [n_gdn, N, h_v, d, d] (and conv
     states fp32 [n_gdn, N, conv_dim, width-1] if asked).  layer_events: one
     torch.cuda.Event (or None) per GDN layer, recorded as soon as that
-    layer's state is written (layer-wise handoff)."""
+    layer's state is written (layer-wise handoff).  packed_weights entries
+    are pack_gdn_layer outputs, or (pack_gdn_layer, pack_ffn) pairs for
+    layers followed by an FFN block of width ffn_dim."""
     desc, _keep, wts, states, conv, n_gdn, T = _group_prepare(
         anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width, rms_eps,
-        l2_eps, max_seqlen, want_conv_state, states, conv_states, layer_events)
+        l2_eps, max_seqlen, want_conv_state, states, conv_states, layer_events, ffn_dim)
     lib = _lib.load()
     ws_bytes = int(lib.sr_replay_group_workspace_bytes(ctypes.byref(desc)))
     if ws_bytes == 0 and n_gdn and T > 0:
@@ -452,14 +489,14 @@ def noalloc_max_bytes() -> int:
 def replay_group_noalloc(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
                          conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None,
                          want_conv_state=False, states=None, conv_states=None,
-                         layer_events=None):
+                         layer_events=None, ffn_dim=0):
     """replay_group without a workspace allocation (sr_replay_group_noalloc):
     the library's static per-GPU workspace is used.  Pass preallocated
     `states` (and `conv_states`) to keep the call free of allocations.
     Calls that overlap on one GPU race."""
     desc, _keep, wts, states, conv, n_gdn, T = _group_prepare(
         anchors, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width, rms_eps,
-        l2_eps, max_seqlen, want_conv_state, states, conv_states, layer_events)
+        l2_eps, max_seqlen, want_conv_state, states, conv_states, layer_events, ffn_dim)
     st = _lib.load().sr_replay_group_noalloc(ctypes.byref(desc), wts, _ptr(anchors),
                                              _ptr(cu_seqlens), _ptr(states), _ptr(conv),
                                              _stream())
@@ -470,13 +507,13 @@ def replay_group_noalloc(anchors, packed_weights, cu_seqlens, layer_kind, h_k, h
 def extend_group(tokens, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, *,
                  initial_states=None, initial_conv_states=None, want_hidden=True,
                  conv_width=4, rms_eps=1e-6, l2_eps=1e-6, max_seqlen=None, states=None,
-                 conv_states=None, workspace=None, layer_events=None):
+                 conv_states=None, workspace=None, layer_events=None, ffn_dim=0):
     """Continue a group from given per-layer states and conv windows over new
     tokens (sr_extend_group).  Returns (states, conv_states, hidden_out fp32
     [T, hidden] or None)."""
     desc, _keep, wts, states, conv, n_gdn, T = _group_prepare(
         tokens, packed_weights, cu_seqlens, layer_kind, h_k, h_v, d, conv_width, rms_eps,
-        l2_eps, max_seqlen, True, states, conv_states, layer_events)
+        l2_eps, max_seqlen, True, states, conv_states, layer_events, ffn_dim)
     dev = tokens.device
     n = cu_seqlens.shape[0] - 1
     if initial_states is not None:

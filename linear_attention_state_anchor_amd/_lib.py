@@ -42,11 +42,11 @@ class GroupDesc(ctypes.Structure):
                 ("conv_width", c_i32), ("rms_eps", ctypes.c_float),
                 ("l2_eps", ctypes.c_float), ("n_seqs", c_i32),
                 ("total_tokens", c_i32), ("max_seqlen", c_i32),
-                ("layer_events", ctypes.POINTER(c_p))]
+                ("layer_events", ctypes.POINTER(c_p)), ("ffn_dim", c_i32)]
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [("packed", c_p)]
+    _fields_ = [("packed", c_p), ("ffn", c_p)]
 
 
 # every symbol the header declares, with (restype, argtypes)
@@ -71,6 +71,8 @@ SIGNATURES = {
     "sr_packed_layer_bytes": (ctypes.c_size_t, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "sr_pack_gdn_layer": (ctypes.c_int, [c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                          c_p, c_p]),
+    "sr_packed_ffn_bytes": (ctypes.c_size_t, [c_i32, c_i32]),
+    "sr_pack_ffn": (ctypes.c_int, [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]),
     "sr_replay_group_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(GroupDesc)]),
     "sr_replay_group": (ctypes.c_int, [ctypes.POINTER(GroupDesc), ctypes.POINTER(LayerWeights),
                                        c_p, c_p, c_p, c_p, c_p, ctypes.c_size_t, c_p]),

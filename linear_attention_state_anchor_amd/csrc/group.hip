@@ -118,6 +118,27 @@ __global__ void pack_wout_kernel(const uint16_t* __restrict__ w, LayerShape L,
   }
 }
 
+// FFN weights: gate, up bf16 [hidden][F] -> W_gu^T fp16 [2F][hidden] with rows
+// alternating in pairs (gate c, up c, gate c+1, up c+1, ...: the layout the
+// EPI_SWIGLU epilogue reads); down bf16 [F][hidden] -> W_down^T fp16
+// [hidden][F]
+__global__ void pack_ffn_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
+                                const uint16_t* __restrict__ wd, int hidden, int F,
+                                _Float16* __restrict__ gu, _Float16* __restrict__ dn) {
+  const size_t total = static_cast<size_t>(hidden) * F;
+  for (size_t e = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; e < total;
+       e += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const int k = static_cast<int>(e / F), c = static_cast<int>(e % F);  // w*[k][c]
+    // gate c at row 4 (c/2) + 2 (c%2), up c right after it
+    const size_t row_g = static_cast<size_t>(4 * (c / 2) + 2 * (c % 2));
+    gu[row_g * hidden + k] = static_cast<_Float16>(bf16_to_f32(wg[e]));
+    gu[(row_g + 1) * hidden + k] = static_cast<_Float16>(bf16_to_f32(wu[e]));
+    // down: e indexes [F][hidden] as well (same count)
+    const int f = static_cast<int>(e / hidden), n = static_cast<int>(e % hidden);
+    dn[static_cast<size_t>(n) * F + f] = static_cast<_Float16>(bf16_to_f32(wd[e]));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // pre-mixer RMSNorm (unit weight): xh_t = fp16(x_t / sqrt(mean_c x_t,c^2 + eps)),
 // one wave per row, 8 consecutive elements per lane and step
@@ -188,6 +209,10 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, const floa
 // accumulation.
 //   EPI_STORE16: C fp16 = acc
 //   EPI_STORE32: C fp32 = acc
+//   EPI_SWIGLU:  B's rows alternate gate and up columns in pairs, so the
+//                4 consecutive results of a lane are (g_c, u_c, g_c+1,
+//                u_c+1); C fp16 [M][N/2] = SiLU(g) * u (the FFN's gated
+//                product, formed in the epilogue)
 // Workgroup tile 256 x 256 x 64, 4 waves of 128 x 128 (16 accumulators of
 // 32x32x16 MFMAs each, held in the accumulation registers); LDS is double
 // buffered, the next k-tile is loaded into registers while the current one
@@ -200,6 +225,7 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, const floa
 // ---------------------------------------------------------------------------
 constexpr int EPI_STORE16 = 0;
 constexpr int EPI_STORE32 = 1;
+constexpr int EPI_SWIGLU = 2;
 constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8;
 constexpr int GGROUP = 8;  // M-tiles per group of the tile order
 constexpr int kXcdG = 8;   // XCDs
@@ -358,10 +384,15 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
         if (n >= N) continue;  // N % 4 == 0: a group of 4 is in or out as a whole
         const size_t ci = static_cast<size_t>(m) * ldc + n;
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        if (EPI == EPI_STORE16)
+        if (EPI == EPI_STORE16) {
           *reinterpret_cast<f16x4*>(static_cast<_Float16*>(C) + ci) = to_f16x4(v);
-        else
+        } else if (EPI == EPI_SWIGLU) {
+          const f16x2 h = {static_cast<_Float16>(silu(v[0]) * v[1]),
+                           static_cast<_Float16>(silu(v[2]) * v[3])};
+          *reinterpret_cast<f16x2*>(static_cast<_Float16*>(C) + static_cast<size_t>(m) * ldc + n / 2) = h;
+        } else {
           *reinterpret_cast<f32x4*>(static_cast<float*>(C) + ci) = v;
+        }
       }
   }
 }
@@ -578,7 +609,9 @@ struct Workspace {
   size_t xres, dres, xh, p, q, k, v, la, be, o, y, ss, sid, total;
 };
 
-Workspace plan(const LayerShape& L, int T) {
+// (the FFN's gated product [T][F] fp16 reuses the projection rows, dead by
+// the time the FFN runs)
+Workspace plan(const LayerShape& L, int T, int ffn_dim) {
   Workspace w{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -590,7 +623,7 @@ Workspace plan(const LayerShape& L, int T) {
   w.xres = take(t * L.hidden * 4);
   w.dres = take(t * L.hidden * 4);
   w.xh = take(t * L.hidden * 2);
-  w.p = take(t * L.n_all() * 2);
+  w.p = take(t * static_cast<size_t>(std::max(L.n_all(), ffn_dim)) * 2);
   w.q = take(t * L.h_k * L.d * 2);
   w.k = take(t * L.h_k * L.d * 2);
   w.v = take(t * L.h_v * L.d * 2);
@@ -616,9 +649,9 @@ hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, 
     const int mm = std::min(mc, M - m_at);
     const int tiles = ((N + GBN - 1) / GBN) * ((mm + GBM - 1) / GBM);
     dim3 grid((tiles + kXcdG - 1) / kXcdG * kXcdG), block(256);
-    void* Cm = EPI == EPI_STORE16
-                   ? static_cast<void*>(static_cast<_Float16*>(C) + static_cast<size_t>(m_at) * ldc)
-                   : static_cast<void*>(static_cast<float*>(C) + static_cast<size_t>(m_at) * ldc);
+    void* Cm = EPI == EPI_STORE32
+                   ? static_cast<void*>(static_cast<float*>(C) + static_cast<size_t>(m_at) * ldc)
+                   : static_cast<void*>(static_cast<_Float16*>(C) + static_cast<size_t>(m_at) * ldc);
     hipLaunchKernelGGL((gemm_kernel<EPI>), grid, block, 0, s, A + static_cast<size_t>(m_at) * lda,
                        lda, Bt, ldb, mm, N, K, Cm, ldc);
     const hipError_t e = hipGetLastError();
@@ -630,13 +663,32 @@ hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, 
 bool shape_ok(const sr_group_desc* d) {
   return d->hidden > 0 && d->hidden % 128 == 0 && d->h_k > 0 && d->h_v > 0 &&
          d->h_v % d->h_k == 0 && (d->d == 64 || d->d == 128) && d->conv_width >= 2 &&
-         d->conv_width <= 8 && d->n_seqs >= 0 && d->total_tokens >= 0;
+         d->conv_width <= 8 && d->n_seqs >= 0 && d->total_tokens >= 0 && d->ffn_dim >= 0 &&
+         d->ffn_dim % 64 == 0;
 }
 
 }  // namespace
 }  // namespace sr
 
 using sr::LayerShape;
+
+extern "C" size_t sr_packed_ffn_bytes(int32_t hidden, int32_t ffn_dim) {
+  if (hidden <= 0 || ffn_dim <= 0) return 0;
+  return sr::align_up(static_cast<size_t>(3) * ffn_dim * hidden * 2, sr::kAlign);
+}
+
+extern "C" int sr_pack_ffn(const void* w_gate, const void* w_up, const void* w_down,
+                           int32_t hidden, int32_t ffn_dim, void* packed, void* stream) {
+  if (!w_gate || !w_up || !w_down || !packed) return SR_EINVAL;
+  if (hidden <= 0 || hidden % 128 != 0 || ffn_dim <= 0 || ffn_dim % 64 != 0) return SR_ESHAPE;
+  if ((reinterpret_cast<uintptr_t>(packed) & (sr::kAlign - 1)) != 0) return SR_EINVAL;
+  _Float16* gu = static_cast<_Float16*>(packed);
+  _Float16* dn = gu + static_cast<size_t>(2 * ffn_dim) * hidden;
+  hipLaunchKernelGGL(sr::pack_ffn_kernel, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+                     static_cast<const uint16_t*>(w_down), hidden, ffn_dim, gu, dn);
+  return hipGetLastError() == hipSuccess ? SR_OK : SR_ELAUNCH;
+}
 
 extern "C" size_t sr_packed_layer_bytes(int32_t hidden, int32_t h_k, int32_t h_v, int32_t d,
                                         int32_t conv_width) {
@@ -673,7 +725,7 @@ extern "C" int sr_pack_gdn_layer(const void* w_in, const void* conv_w, const voi
 extern "C" size_t sr_replay_group_workspace_bytes(const sr_group_desc* d) {
   if (!d || !sr::shape_ok(d)) return 0;
   LayerShape L{d->hidden, d->h_k, d->h_v, d->d, d->conv_width};
-  return sr::plan(L, d->total_tokens).total;
+  return sr::plan(L, d->total_tokens, d->ffn_dim).total;
 }
 
 namespace sr {
@@ -707,7 +759,7 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
     if (!weights[i].packed) return SR_EINVAL;
   LayerShape L{d->hidden, d->h_k, d->h_v, d->d, d->conv_width};
   const int T = d->total_tokens;
-  const sr::Workspace W = sr::plan(L, T);
+  const sr::Workspace W = sr::plan(L, T, d->ffn_dim);
   if (T > 0 && (!anchors || !workspace)) return SR_EINVAL;
   if (T > 0 && workspace_bytes < W.total) return SR_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (sr::kAlign - 1)) != 0) return SR_EINVAL;
@@ -739,6 +791,24 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
                        d->n_seqs, T, sst, sid);
     if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
   }
+  // The residual stream x starts as the anchors (bf16); each residual add
+  // (x + mixer or FFN output, fp32, in dres) happens inside the RMSNorm that
+  // reads it, which writes the sum to xres.
+  bool x_is_anchors = true;
+  auto norm = [&](bool add) -> bool {
+    const dim3 rgrid((T + 3) / 4);
+    if (!add)
+      hipLaunchKernelGGL((sr::rms_norm_kernel<sr::BF16, false>), rgrid, dim3(256), 0, s, anchors,
+                         nullptr, T, d->hidden, d->rms_eps, nullptr, xh);
+    else if (x_is_anchors)
+      hipLaunchKernelGGL((sr::rms_norm_kernel<sr::BF16, true>), rgrid, dim3(256), 0, s, anchors,
+                         dres, T, d->hidden, d->rms_eps, xres, xh);
+    else
+      hipLaunchKernelGGL((sr::rms_norm_kernel<sr::F32, true>), rgrid, dim3(256), 0, s,
+                         static_cast<const void*>(xres), dres, T, d->hidden, d->rms_eps, xres, xh);
+    if (add) x_is_anchors = false;
+    return hipGetLastError() == hipSuccess;
+  };
   for (int li = 0; li < n_gdn; ++li) {
     const bool is_last = li == n_gdn - 1;
     // the mixer's outputs are formed for every layer but the last, and for
@@ -751,21 +821,10 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
     const _Float16* wout = reinterpret_cast<const _Float16*>(pk + L.win_bytes() + L.conv_bytes());
     float* st = states + state_stride * li;
     if (T > 0) {
-      // x of this layer: the anchors (bf16) for the first; after that the
-      // previous x plus the previous layer's output projection (dres), which
-      // this kernel adds and stores into the fp32 residual stream (xres);
-      // xh = RMSNorm(x) in fp16, the A operand of the projection
-      const dim3 rgrid((T + 3) / 4);
-      if (li == 0)
-        hipLaunchKernelGGL((sr::rms_norm_kernel<sr::BF16, false>), rgrid, dim3(256), 0, s, anchors,
-                           nullptr, T, d->hidden, d->rms_eps, nullptr, xh);
-      else if (li == 1)
-        hipLaunchKernelGGL((sr::rms_norm_kernel<sr::BF16, true>), rgrid, dim3(256), 0, s, anchors,
-                           dres, T, d->hidden, d->rms_eps, xres, xh);
-      else
-        hipLaunchKernelGGL((sr::rms_norm_kernel<sr::F32, true>), rgrid, dim3(256), 0, s,
-                           static_cast<const void*>(xres), dres, T, d->hidden, d->rms_eps, xres, xh);
-      if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+      // x of this layer: the anchors for the first, after that the residual
+      // stream plus the previous block's output (dres); xh = RMSNorm(x) in
+      // fp16, the A operand of the projection
+      if (!norm(li > 0)) return SR_ELAUNCH;
       // the last layer needs k|v|a|b for its state, and q as well when its
       // conv window is returned (q follows the state prefix in the packing)
       const int N = full ? L.n_all()
@@ -839,11 +898,25 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
     // the residual add happens in the next layer's RMSNorm
     hipError_t e = sr::gemm<sr::EPI_STORE32>(yb, K2, wout, K2, T, d->hidden, K2, dres, d->hidden, s);
     if (e != hipSuccess) return SR_ELAUNCH;
+    // FFN block after the mixer (not after the last layer of a replay: its
+    // output is never used there): x <- x + W_down (SiLU(xh W_g) * (xh W_u))
+    if (d->ffn_dim > 0 && weights[li].ffn) {
+      const int F = d->ffn_dim;
+      const _Float16* wgu = static_cast<const _Float16*>(weights[li].ffn);
+      const _Float16* wdn = wgu + static_cast<size_t>(2 * F) * d->hidden;
+      _Float16* hb = P;  // [T][F] fp16, the projection rows are dead here
+      if (!norm(true)) return SR_ELAUNCH;
+      if (sr::gemm<sr::EPI_SWIGLU>(xh, d->hidden, wgu, d->hidden, T, 2 * F, d->hidden, hb, F, s) !=
+          hipSuccess)
+        return SR_ELAUNCH;
+      if (sr::gemm<sr::EPI_STORE32>(hb, F, wdn, F, T, d->hidden, F, dres, d->hidden, s) != hipSuccess)
+        return SR_ELAUNCH;
+    }
     if (is_last) {
-      // the group's output: the last layer's input plus its mixer output
+      // the group's output: the residual stream plus the last block's output
       const size_t count = static_cast<size_t>(T) * d->hidden;
       const int blocks = static_cast<int>(std::min<size_t>(4096, (count + 255) / 256));
-      if (li == 0)
+      if (x_is_anchors)
         hipLaunchKernelGGL(sr::residual_out_kernel<sr::BF16>, dim3(blocks), dim3(256), 0, s, anchors,
                            dres, count, hidden_out);
       else

@@ -46,13 +46,14 @@ class GroupReplayGraphs:
 
     def __init__(self, packed_weights, layer_kind, h_k, h_v, d, hidden, *,
                  buckets=(512, 1024, 2048, 4096, 8192), max_requests=64, conv_width=4,
-                 want_conv_state=False, device="cuda"):
+                 want_conv_state=False, ffn_dim=0, device="cuda"):
         self.w = list(packed_weights)
         self.kinds = [int(x) for x in layer_kind]
         self.n_gdn = sum(1 for x in self.kinds if x == SR_LAYER_GDN)
         self.h_k, self.h_v, self.d, self.hidden = h_k, h_v, d, hidden
         self.conv_width = conv_width
         self.want_conv = want_conv_state
+        self.ffn_dim = ffn_dim
         self.max_requests = max_requests
         self.sizes = sorted(int(b) for b in buckets)
         self.device = torch.device(device)
@@ -67,12 +68,14 @@ class GroupReplayGraphs:
     def _replay(self, bk):
         replay_group(bk.anchors, self.w, bk.cu, self.kinds, self.h_k, self.h_v, self.d,
                      conv_width=self.conv_width, want_conv_state=self.want_conv,
-                     states=bk.states, conv_states=bk.conv, workspace=bk.workspace)
+                     states=bk.states, conv_states=bk.conv, workspace=bk.workspace,
+                     ffn_dim=self.ffn_dim)
 
     def _capture(self, size):
         conv_dim = (2 * self.h_k + self.h_v) * self.d if self.want_conv else 0
         ws = group_workspace_bytes(size, self.hidden, self.h_k, self.h_v, self.d,
-                                   self.conv_width, self.max_requests + 1, self.kinds)
+                                   self.conv_width, self.max_requests + 1, self.kinds,
+                                   self.ffn_dim)
         bk = _Bucket(size, self.max_requests, self.hidden, self.n_gdn, self.h_v, self.d,
                      conv_dim, self.conv_width, ws, self.device)
         # one eager run on a side stream (loads the code objects, settles

@@ -303,6 +303,14 @@ def output_path(o, z, w_out, eps=1e-6):
     return y.reshape(T, -1) @ _f64(w_out)
 
 
+def ffn_block(x, w_gate, w_up, w_down, eps=1e-6):
+    """Pre-norm feed-forward block: x + (SiLU(x^ W_gate) * (x^ W_up)) W_down
+    with x^ = RMSNorm(x), unit weight.  The pages give no FFN form; a SwiGLU
+    FFN of the family the pages evaluate is taken."""
+    xh = rmsnorm_rows(np.asarray(x, dtype=np.float64), eps)
+    return x + (silu(xh @ _f64(w_gate)) * (xh @ _f64(w_up))) @ _f64(w_down)
+
+
 def replay_group(anchors, weights, cu_seqlens, layer_kind, h_k, h_v, d,
                  rms_eps=1e-6, l2_eps=1e-6, return_trace=False):
     """Replay one group of linear-attention layers from its entry anchors.
@@ -352,6 +360,11 @@ def extend_group(tokens, weights, cu_seqlens, layer_kind, h_k, h_v, d, initial_s
             trace.append(dict(x=x, **fe, o=o))
         if full:
             x = x + output_path(o, fe["z"], w.w_out, rms_eps)
+            # the FFN after the mixer ("Tail-Replay", section 3: replay omits
+            # the group's final FFN -- it runs for the last layer only when
+            # the group's output is asked for)
+            if getattr(w, "w_gate", None) is not None:
+                x = ffn_block(x, w.w_gate, w.w_up, w.w_down, rms_eps)
         if last and want_hidden:
             hidden = x
     st = np.stack(states) if states else np.zeros((0,))

@@ -27,7 +27,7 @@ import numpy as np
 __all__ = [
     "to_bf16_bits", "bf16_bits_to_f32", "widen", "GdnCase", "gdn_case",
     "config_c1", "config_c2", "config_c3", "GroupCase", "group_weights",
-    "config_c4", "config_c5", "PoolCase", "suffix_pool_case", "CONFIG_SEEDS",
+    "config_c4", "config_c5", "PoolCase", "suffix_pool_case", "CONFIG_SEEDS", "FFN_DIM",
 ]
 
 CONFIG_SEEDS = {1: 101, 2: 102, 3: 103, 4: 104, 5: 105}
@@ -212,10 +212,14 @@ GDN, FA = 0, 1
 
 @dataclass
 class GroupWeights:
-    """bf16 weights of one GDN layer (bit patterns)."""
+    """bf16 weights of one GDN layer (bit patterns), with an optional FFN
+    block after it."""
     w_in: np.ndarray    # [hidden][n_in]  columns q | k | v | z | a | b
     conv_w: np.ndarray  # [conv_dim][width]  over the q|k|v channels
     w_out: np.ndarray   # [h_v*d_v][hidden]
+    w_gate: np.ndarray | None = None  # [hidden][ffn]
+    w_up: np.ndarray | None = None    # [hidden][ffn]
+    w_down: np.ndarray | None = None  # [ffn][hidden]
 
 
 @dataclass
@@ -241,12 +245,13 @@ class GroupCase:
 
 
 def group_weights(rng, hidden, h_k, h_v, d, conv_width=4, w_std=0.02,
-                  conv_std=0.5) -> GroupWeights:
+                  conv_std=0.5, ffn_dim=0) -> GroupWeights:
     """Random-init bf16 weights of one GDN layer.
 
     Projection columns: q (h_k*d) | k (h_k*d) | v (h_v*d) | z (h_v*d) |
     a (h_v) | b (h_v), all N(0, w_std^2).  Conv taps N(0, conv_std^2) over the
-    q|k|v channels.  Output projection N(0, w_std^2).
+    q|k|v channels.  Output projection N(0, w_std^2).  With ffn_dim > 0,
+    FFN gate, up and down weights N(0, w_std^2) are drawn after the others.
     """
     n_in = 2 * h_k * d + 2 * h_v * d + 2 * h_v
     conv_dim = 2 * h_k * d + h_v * d
@@ -258,28 +263,41 @@ def group_weights(rng, hidden, h_k, h_v, d, conv_width=4, w_std=0.02,
     w_out = to_bf16_bits(rng.standard_normal((h_v * d, hidden),
                                              dtype=np.float32)
                          * np.float32(w_std))
-    return GroupWeights(w_in=w_in, conv_w=conv_w, w_out=w_out)
+    gw = GroupWeights(w_in=w_in, conv_w=conv_w, w_out=w_out)
+    if ffn_dim:
+        draw = lambda shape: to_bf16_bits(rng.standard_normal(shape, dtype=np.float32)
+                                          * np.float32(w_std))
+        gw.w_gate = draw((hidden, ffn_dim))
+        gw.w_up = draw((hidden, ffn_dim))
+        gw.w_down = draw((ffn_dim, hidden))
+    return gw
 
 
-def _group(lens, seed, hidden, h_k, h_v, d, layer_kind, conv_width=4):
+def _group(lens, seed, hidden, h_k, h_v, d, layer_kind, conv_width=4, ffn_dim=0):
     rng = np.random.default_rng(seed)
     T = int(sum(lens))
     anchors = to_bf16_bits(rng.standard_normal((T, hidden), dtype=np.float32))
-    weights = [group_weights(rng, hidden, h_k, h_v, d, conv_width)
+    weights = [group_weights(rng, hidden, h_k, h_v, d, conv_width, ffn_dim=ffn_dim)
                for kind in layer_kind if kind == GDN]
     cu = np.zeros(len(lens) + 1, dtype=np.int32)
     if lens:
         cu[1:] = np.cumsum(np.asarray(lens, dtype=np.int64)).astype(np.int32)
     return GroupCase(anchors=anchors, cu_seqlens=cu, layer_kind=list(layer_kind),
                      weights=weights, hidden=hidden, h_k=h_k, h_v=h_v, d=d,
-                     conv_width=conv_width, meta={"seed": seed, "lens": list(lens)})
+                     conv_width=conv_width, meta={"seed": seed, "lens": list(lens),
+                                                  "ffn_dim": ffn_dim})
+
+
+FFN_DIM = 9728  # FFN width taken for the hidden-2560 layers (see the group oracle)
 
 
 def config_c4(seed=CONFIG_SEEDS[4], n_seqs=4, suffix=1638, hidden=2560,
-              h_k=16, h_v=32, d=128) -> GroupCase:
+              h_k=16, h_v=32, d=128, ffn_dim=0) -> GroupCase:
     """Replay group: 3 GDN layers then a skipped full-attention layer,
-    hidden 2560, 4 requests x 1638 anchors (5 % of 32K)."""
-    g = _group([suffix] * n_seqs, seed, hidden, h_k, h_v, d, [GDN, GDN, GDN, FA])
+    hidden 2560, 4 requests x 1638 anchors (5 % of 32K); with ffn_dim, an
+    FFN block after each GDN layer."""
+    g = _group([suffix] * n_seqs, seed, hidden, h_k, h_v, d, [GDN, GDN, GDN, FA],
+               ffn_dim=ffn_dim)
     g.meta["name"] = f"group {n_seqs}x{suffix} D{hidden} 3xGDN+FA"
     return g
 

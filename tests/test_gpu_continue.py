@@ -94,22 +94,28 @@ def _split(g, cut):
     return pre, tail, cu_pre, cu_tail
 
 
-@pytest.mark.parametrize("hidden,hk,hv,d", [(256, 2, 4, 128), (256, 2, 4, 64),
-                                             (2560, 16, 32, 128)])
-def test_extend_group_continues_the_replay(hidden, hk, hv, d):
+@pytest.mark.parametrize("hidden,hk,hv,d,F", [(256, 2, 4, 128, 0), (256, 2, 4, 64, 0),
+                                               (2560, 16, 32, 128, 0), (256, 2, 4, 128, 320)])
+def test_extend_group_continues_the_replay(hidden, hk, hv, d, F):
+    """Also with FFN blocks (F > 0): the last layer's FFN, skipped by the
+    prefix replay, runs in the extension, whose output includes it."""
     import torch
     import linear_attention_state_anchor_amd as sr
-    print(f"[continue] group hidden={hidden} hk={hk} hv={hv} d={d}", flush=True)
+    print(f"[continue] group hidden={hidden} hk={hk} hv={hv} d={d} ffn={F}", flush=True)
     lens = [300, 70, 65, 2]
     cut = [200, 1, 64, 2]              # the last request has no new tokens
-    g = _group(lens, 91 + d, hidden, hk, hv, d, [GDN, GDN, GDN, FA])
-    packed = [sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), hk, hv, d)
-              for w in g.weights]
+    g = _group(lens, 91 + d, hidden, hk, hv, d, [GDN, GDN, GDN, FA], ffn_dim=F)
+    packed = []
+    for w in g.weights:
+        mix = sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), hk, hv, d)
+        packed.append((mix, sr.pack_ffn(to_dev(w.w_gate), to_dev(w.w_up), to_dev(w.w_down)))
+                      if F else mix)
     pre, tail, cu_pre, cu_tail = _split(g, cut)
     S_pre, C_pre = sr.replay_group(to_dev(g.anchors[pre]), packed, to_dev(cu_pre), g.layer_kind,
-                                   hk, hv, d, want_conv_state=True)
+                                   hk, hv, d, want_conv_state=True, ffn_dim=F)
     S, C, H = sr.extend_group(to_dev(g.anchors[tail]), packed, to_dev(cu_tail), g.layer_kind,
-                              hk, hv, d, initial_states=S_pre, initial_conv_states=C_pre)
+                              hk, hv, d, initial_states=S_pre, initial_conv_states=C_pre,
+                              ffn_dim=F)
     torch.cuda.synchronize()
     Sr, Cr, Hr, _ = oracle.extend_group(g.anchors, g.weights, g.cu_seqlens, g.layer_kind,
                                         hk, hv, d)

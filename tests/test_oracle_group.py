@@ -278,3 +278,38 @@ def test_extend_group_equals_the_whole_run():
     S_bad, _, _, _ = oracle.extend_group(g.anchors[tail_rows], g.weights, cu_tail, g.layer_kind,
                                          2, 4, 4, initial_states=S_pre)
     assert oracle.rel_fro(S_bad, S_full) > 1e-6
+
+
+# ---------------------------------------------------------------------------
+# FFN blocks between the group's GDN layers ("Tail-Replay", section 3: the
+# group's final FFN is omitted from replay).  The pages give no FFN form; the
+# SwiGLU block is a reading, pinned here only to its structure.
+# ---------------------------------------------------------------------------
+def test_ffn_block_structure():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, 16))
+    wg, wu = rng.standard_normal((16, 32)), rng.standard_normal((16, 32))
+    wd = rng.standard_normal((32, 16))
+    f = lambda a, b, c: oracle.ffn_block(x, a, b, c)
+    np.testing.assert_array_equal(f(wg, wu, np.zeros_like(wd)), x)      # no down: identity
+    np.testing.assert_array_equal(f(np.zeros_like(wg), wu, wd), x)      # SiLU(0) = 0
+    # linear in the down projection, and the gate enters through SiLU
+    np.testing.assert_allclose(f(wg, wu, 2 * wd) - x, 2 * (f(wg, wu, wd) - x), rtol=1e-12)
+    xh = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6)
+    g, u = xh @ wg, xh @ wu
+    np.testing.assert_allclose(f(wg, wu, wd), x + (special.expit(g) * g * u) @ wd, rtol=1e-12)
+
+
+def test_group_ffn_only_reaches_later_layers():
+    """An FFN after layer l changes the states of layers after l only, and
+    the last layer's FFN changes no state at all (skipped in replay)."""
+    g = _group([20, 7], 23, 16, 2, 4, 4, [GDN, GDN, GDN], ffn_dim=32)
+    plain = _group([20, 7], 23, 16, 2, 4, 4, [GDN, GDN, GDN])
+    S_f, _ = oracle.replay_group(g.anchors, g.weights, g.cu_seqlens, g.layer_kind, 2, 4, 4)
+    S_p, _ = oracle.replay_group(plain.anchors, plain.weights, g.cu_seqlens, g.layer_kind, 2, 4, 4)
+    np.testing.assert_array_equal(S_f[0], S_p[0])
+    assert oracle.rel_fro(S_f[1], S_p[1]) > 1e-6 and oracle.rel_fro(S_f[2], S_p[2]) > 1e-6
+    w_last = list(g.weights)
+    w_last[2] = type(w_last[2])(**{**w_last[2].__dict__, "w_down": w_last[2].w_down * 0})
+    S_l, _ = oracle.replay_group(g.anchors, w_last, g.cu_seqlens, g.layer_kind, 2, 4, 4)
+    np.testing.assert_array_equal(S_l, S_f)
