@@ -507,9 +507,63 @@ def error_vs_k(to_dev, n_req=8, ks=(16, 32, 64, 128, 256, 512)):
         err = [float(torch.linalg.vector_norm(S[l] - full[l]) / torch.linalg.vector_norm(full[l]))
                for l in range(full.shape[0])]
         rows.append({"k": label, "rel_fro_per_layer": err})
-    return {"workload": f"{n_req} hits of the varlen workload (m = {list(map(int, m))}), "
-                        "3-layer group, full-prefix vs suffix replay, all on the GPU",
-            "rows": rows}
+    out = {"group": {"workload": f"{n_req} hits of the varlen workload (m = "
+                                 f"{list(map(int, m))}), 3-layer group, random-init gates "
+                                 f"(mean alpha about 0.5), full-prefix vs suffix replay, all "
+                                 f"on the GPU",
+                     "rows": rows}}
+    out["slow_decay"] = error_vs_k_slow_decay(to_dev, ks)
+    return out
+
+
+def error_vs_k_slow_decay(to_dev, ks, n_seqs=4, m=16384, h_k=4, h_v=8):
+    """Replay error against k for one GDN layer whose gates forget slowly:
+    alpha ~ U[0.90, 0.999] per token and head (the scalar-decay recipe), so
+    the product of the replayed alphas spans about 0.4 (k = 16) to below
+    1e-6 (k = 256).  Gated delta rule (unit keys, beta = sigmoid(N(0,1))) and
+    scalar decay (beta = 1, keys N(0,1)).  Per k: the relative Frobenius
+    error of the suffix state against the full-prefix state, and the bound
+    (product of the replayed alphas) x |S_(m-k)| / |S_m| the recurrence
+    gives (an equality without the erase term)."""
+    import numpy as np
+    import torch
+    import linear_attention_state_anchor_amd as sr
+    from replay_inputs import gdn_case
+
+    res = {}
+    for name, kw in (("gated_delta_rule", dict(normalize_k=True, beta="sigmoid", erase=True)),
+                     ("scalar_decay", dict(normalize_k=False, beta="none", erase=False))):
+        c = gdn_case([m] * n_seqs, h_k, h_v, 128, "bf16", seed=77, alpha=("uniform", 0.90, 0.999),
+                     **kw)
+        k_all, v_all, a_all = to_dev(c.k), to_dev(c.v), to_dev(c.alpha)
+        b_all = None if c.beta is None else to_dev(c.beta)
+        la = np.log(c.alpha.astype(np.float64)).reshape(n_seqs, m, h_v)
+
+        def state(lo, hi):
+            idx = torch.cat([torch.arange(i * m + lo, i * m + hi, device="cuda:0")
+                             for i in range(n_seqs)])
+            cu = to_dev(np.arange(0, n_seqs * (hi - lo) + 1, hi - lo, dtype=np.int32))
+            S, _ = sr.gdn_replay_state(None, k_all[idx], v_all[idx], a_all[idx],
+                                       None if b_all is None else b_all[idx], cu, erase=c.erase,
+                                       alpha_is_log=False, want_o=False)
+            return S.double()
+
+        full = state(0, m)
+        nf = float(torch.linalg.vector_norm(full))
+        rows = []
+        for kk in list(ks) + [int(np.ceil(0.05 * m)), int(np.ceil(0.10 * m))]:
+            S = state(m - kk, m)
+            err = float(torch.linalg.vector_norm(S - full)) / nf
+            head = state(0, m - kk)
+            # bound per (sequence, head): prod(alpha over the suffix) |S_(m-k)|
+            pa = np.exp(la[:, m - kk:, :].sum(axis=1))               # [n_seqs][h_v]
+            hn = torch.linalg.vector_norm(head, dim=(2, 3)).cpu().numpy()
+            bound = float(np.sqrt(np.sum((pa * hn) ** 2))) / nf
+            rows.append({"k": kk, "rel_fro": err, "bound": bound,
+                         "mean_prod_alpha": float(pa.mean())})
+        res[name] = {"workload": f"{n_seqs} x {m} tokens, {h_k} key / {h_v} value heads, d=128, "
+                                 f"bf16, alpha ~ U[0.90, 0.999]", "rows": rows}
+    return res
 
 
 def main():

@@ -90,3 +90,87 @@ def test_group_error_shrinks_with_k_and_matches_oracle():
     assert np.all(errs[-1] == 0.0)           # k >= m: the same replay
     for l in range(2):
         assert errs[0, l] > errs[2, l]       # longer suffix, smaller error
+
+
+@pytest.mark.parametrize("erase", [True, False])
+def test_slow_decay_error_vs_k_matches_oracle(erase):
+    """alpha ~ U[0.90, 0.999] (slow forgetting): the replay error falls from
+    tens of percent at k = 16 to the rounding floor at k = 256.  The GPU's
+    error at each k matches the oracle's (fp64) error."""
+    import torch
+    import linear_attention_state_anchor_amd as sr
+    m, ks = 2048, (16, 64, 256)
+    c = gdn_case([m, m], 2, 4, 128, "bf16", seed=78, alpha=("uniform", 0.90, 0.999),
+                 normalize_k=erase, beta="sigmoid" if erase else "none", erase=erase)
+    print(f"[replay-error] slow decay erase={erase}", flush=True)
+
+    def rows(lo):
+        return np.concatenate([np.arange(i * m + lo, (i + 1) * m) for i in range(2)])
+
+    def cu(L):
+        return np.array([0, L, 2 * L], np.int32)
+
+    def gpu(lo):
+        r = rows(lo)
+        S, _ = sr.gdn_replay_state(None, to_dev(c.k[r]), to_dev(c.v[r]), to_dev(c.alpha[r]),
+                                   None if c.beta is None else to_dev(c.beta[r]),
+                                   to_dev(cu(m - lo)), erase=erase, want_o=False)
+        torch.cuda.synchronize()
+        return to_np(S)
+
+    def orc(lo):
+        r = rows(lo)
+        S, _ = oracle.gdn(None, c.k[r], c.v[r], c.alpha[r], None if c.beta is None else c.beta[r],
+                          cu(m - lo), 2, 4, alpha_is_log=False, erase=erase, want_o=False)
+        return S
+
+    full_g, full_o = gpu(0), orc(0)
+    prev = None
+    for k in ks:
+        eg = rel_fro(gpu(m - k), full_g)
+        eo = rel_fro(orc(m - k), full_o)
+        print(f"    k={k}: gpu {eg:.4e} oracle {eo:.4e}", flush=True)
+        assert abs(eg - eo) <= 0.05 * eo + 3e-3
+        if prev is not None:
+            assert eo < prev
+        prev = eo
+    assert rel_fro(orc(m - 16), full_o) > 0.05     # slow forgetting: k = 16 is far off
+
+
+def test_varlen_group_error_vs_k_two_requests_matches_oracle():
+    """Two hits of the 64-hit varlen workload (the two shortest prefixes, to
+    keep the fp64 full-prefix replay short): GPU and oracle replay errors at
+    k = 16, 64 and ceil(0.05 m) against the full-prefix states of the group."""
+    import torch
+    import linear_attention_state_anchor_amd as sr
+    from replay_inputs import PAGE, config_c5
+    pc, wts = config_c5()
+    sel = list(np.argsort(pc.matched_len)[:2])
+    print(f"[replay-error] varlen requests {sel} m={[int(pc.matched_len[i]) for i in sel]}",
+          flush=True)
+    packed = [sr.pack_gdn_layer(to_dev(w.w_in), to_dev(w.conv_w), to_dev(w.w_out), 16, 32, 128)
+              for w in wts]
+    kinds = [GDN, GDN, GDN, FA]
+    rng = np.random.default_rng(9)
+    m = [int(pc.matched_len[i]) for i in sel]
+    # the two prefixes' anchors (bf16 ~ N(0,1)), page structure irrelevant here
+    prefixes = [pc.pool_pages(pc.page_table[i][:(mi + PAGE - 1) // PAGE]).reshape(-1, 2560)[:mi]
+                for i, mi in zip(sel, m)]
+
+    def run(klist):
+        parts = [p[len(p) - k:] for p, k in zip(prefixes, klist)]
+        a = np.concatenate(parts)
+        cu = np.concatenate([[0], np.cumsum(klist)]).astype(np.int32)
+        S = sr.replay_group(to_dev(a), packed, to_dev(cu), kinds, 16, 32, 128)
+        torch.cuda.synchronize()
+        Sr, _ = oracle.replay_group(a, wts, cu, kinds, 16, 32, 128)
+        return to_np(S), Sr
+
+    full_g, full_o = run(m)
+    for label, klist in (("16", [16, 16]), ("64", [64, 64]),
+                         ("ceil(0.05m)", [int(np.ceil(0.05 * x)) for x in m])):
+        Sg, So = run(klist)
+        for l in range(3):
+            eg, eo = rel_fro(Sg[l], full_g[l]), rel_fro(So[l], full_o[l])
+            print(f"    k={label} layer {l}: gpu {eg:.4e} oracle {eo:.4e}", flush=True)
+            assert abs(eg - eo) <= 0.1 * eo + 3e-3
