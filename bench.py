@@ -671,6 +671,17 @@ def main():
         entry, seqs, S_ref, o_ref = cpu_baseline(case, args.cpu_budget)
         line["cpu_baseline"] = entry
         line["parity"] = parity_vs_oracle(S, o, case, seqs, S_ref, o_ref)
+    if not args.no_group:
+        # the same headline launch once more at the end of the run, after
+        # seconds of other GPU work, as a check that `value` (timed first,
+        # after its warm-up launches) is not an artefact of the GPU's state
+        ts = time_steps(step, args.steps, 10)
+        line["steady_state"] = {
+            "note": "headline launch re-timed at the end of the run, after the other lines' "
+                    "GPU work",
+            "ms_per_step": ts["mean_ms"], "median_ms": ts["median_ms"],
+            "replayed_tokens_per_s": T / (ts["mean_ms"] / 1e3),
+            "hbm_frac": byts / (ts["mean_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS}
     if args.copy_calib:
         src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
