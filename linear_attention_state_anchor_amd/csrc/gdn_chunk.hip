@@ -15,8 +15,9 @@
 // blocks.  With A = diag(b) A~ (A~ without the b_t factor) and
 // R~ = V - diag(e^G) K S^T, block row i reads
 //     U_i = (I + A_ii)^{-1} diag(b_i) (R~_i - sum_{m<i} A~_im U_m):
-// the four 16x16 diagonal blocks are inverted in fp32 (one wave each) and
-// stored with their columns scaled by b, the off-diagonal tiles hold -A~, so
+// the four 16x16 diagonal blocks are inverted on the matrix cores at about
+// fp32 accuracy (one wave each, see chunk_tiles) and stored with their
+// columns scaled by b, the off-diagonal tiles hold -A~, so
 // neither the right-hand side nor the off-diagonal tiles carry b; all
 // products run on the matrix cores with register-resident operands.
 // Solving for U directly (rather than for the S-independent pair
@@ -102,7 +103,6 @@ struct ChunkSmem {
   float dec[HP][kC];                 // e^{G_C - G_t}
   float beta[HP][kC];                // b_t (0 past the end of the sequence)
   _Float16 td[HP][4 * 16 * 16];      // (I + A_bb)^{-1} diag(b), row-major per block
-  float dg[HP][4 * 16 * 16];         // A_bb, fp32, row-major per block
   _Float16 a[HP][kC * kAS];          // -A~ (strictly lower off-diagonal blocks)
   _Float16 pqk[HP][kC * kPS];        // scale * P o (Q K^T)
   _Float16 q[kC * kQS];              // Q rows
@@ -227,6 +227,32 @@ __device__ __forceinline__ float raw_to_f32<F16>(uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
 
+// fp32 tile as fp16 hi + lo parts (x - hi is exact in fp32), for products
+// at about fp32 accuracy on the fp16 matrix cores.  The residual is written
+// as an FMA with fp16 and fp32 operands rounded once to fp16, which is one
+// mixed-precision instruction per element.
+struct SplitF16 {
+  f16x4 h, l;
+};
+__device__ __forceinline__ SplitF16 split_f16(f32x4 x) {
+  SplitF16 s;
+  float m1 = -1.0f;  // opaque, so the FMA is not folded into a subtraction
+  asm("" : "+v"(m1));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    s.h[r] = static_cast<_Float16>(x[r]);
+    s.l[r] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(s.h[r]), m1, x[r]));
+  }
+  return s;
+}
+// a^T b + c for tiles a, b in the 16x16 accumulator layout (hi*hi + hi*lo +
+// lo*hi, small terms first)
+__device__ __forceinline__ f32x4 mfma_split(const SplitF16& a, const SplitF16& b, f32x4 c) {
+  c = mfma16x16x16(a.l, b.h, c);
+  c = mfma16x16x16(a.h, b.l, c);
+  return mfma16x16x16(a.h, b.h, c);
+}
+
 // Tile jobs of wave W for one chunk.  Waves 0..3 of each head form the
 // diagonal blocks A_bb (erase mode; b = the wave within the head) and invert
 // I + A_bb.  The 16 other tiles are shared jobs: with 4 waves, wave W takes
@@ -310,8 +336,9 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
   }
   tr_keep(kl);
   if (WANT_O) tr_keep(ql);
-  // epilogues: masked, decay-weighted tiles to LDS (the diagonal A block in
-  // fp32 for the inverse)
+  // epilogues: masked, decay-weighted tiles to LDS (the diagonal A block
+  // stays in registers for the inverse)
+  f32x4 nd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < NS; ++q) {
     if (!slot_on(q)) continue;
@@ -324,7 +351,7 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
         const int row = 16 * slot_tr(q) + 4 * lg + r;
         const float val = f[q][hh][r] * acc[q][r];
         if (q == 0)
-          sm.dg[HW][WQ * 256 + (4 * lg + r) * 16 + lr] = val;
+          nd[r] = val;
         else if (slot_kk(q))
           sm.a[hd][row * kAS + kperm(col)] = static_cast<_Float16>(val);
         else
@@ -333,33 +360,72 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
     }
   }
   if (kDiag) {
-    // (I + A_bb)^{-1} by forward substitution in fp32, lane column lr; the
-    // block's rows come back from LDS as broadcast reads (this wave wrote
-    // them, so no barrier is needed).  Only one lane group does the work:
-    // a broadcast read returns data to every active lane, so four redundant
-    // groups would quadruple the LDS return traffic.
-    const int c = lr;
-    const float* ab = &sm.dg[HW][WQ * 256];
-    float x[16];
+    // T = (I + N)^{-1} for this wave's diagonal block N = A_bb (strictly
+    // lower, 16 x 16), on the matrix cores.  N is held in the accumulator
+    // layout: lane (lr, lg) has N[4 lg + r][lr], r = 0..3.  Split N = D + L
+    // into its 4 x 4 diagonal blocks D and the strictly block-lower rest L;
+    // then I + N = (I + D)(I + M) with M = (I + D)^{-1} L, and since M is
+    // strictly block-lower over 4 blocks (M^4 = 0)
+    //     T = (I + M)^{-1} (I + D)^{-1},  (I + M)^{-T} = I - Z + Z^2 - Z^3,
+    //     Z = M^T.
+    // (I + D)^{-1} comes in closed form from the six entries of each 4 x 4
+    // block, which sit in one quad of lanes (the quad whose columns meet the
+    // lane group's rows) and are broadcast within it by DPP.  A product
+    // mfma(a, b) of two operands held in the accumulator layout of X and Y
+    // is X^T Y, so every operand below is an accumulator tile; each is split
+    // into fp16 hi + lo parts (three MFMAs per product), which keeps the
+    // result at fp32 accuracy before its one fp16 rounding.  The series has
+    // only four terms of 4 x 4 block structure, so it does not cancel
+    // catastrophically even for a block of identical keys.
+    const int j = lr & 3;                    // column within the 4 x 4 block
+    const bool dblk = (lr >> 2) == lg;       // the lane's rows meet its column's block
+    const bool lblk = (lr >> 2) < lg;        // strictly block-lower position
+    const float e10 = dpp_f32<0x00, 0xf>(nd[1]), e20 = dpp_f32<0x00, 0xf>(nd[2]);
+    const float e30 = dpp_f32<0x00, 0xf>(nd[3]), e21 = dpp_f32<0x55, 0xf>(nd[2]);
+    const float e31 = dpp_f32<0x55, 0xf>(nd[3]), e32 = dpp_f32<0xaa, 0xf>(nd[3]);
+    // (I + D_blk)^{-1}, unit lower triangular: entries i_rj, r > j
+    const float i10 = -e10, i21 = -e21, i32 = -e32;
+    const float i20 = fmaf(e21, e10, -e20);
+    const float i31 = fmaf(e32, e21, -e31);
+    const float i30 = fmaf(-e32, i20, fmaf(-e31, i10, -e30));
+    f32x4 di, dt, id, lm;  // (I + D)^{-1}, its transpose, I, L (accumulator layout)
+    di[0] = j == 0 ? 1.0f : 0.0f;
+    di[1] = j == 0 ? i10 : j == 1 ? 1.0f : 0.0f;
+    di[2] = j == 0 ? i20 : j == 1 ? i21 : j == 2 ? 1.0f : 0.0f;
+    di[3] = j == 0 ? i30 : j == 1 ? i31 : j == 2 ? i32 : 1.0f;
+    dt[0] = j == 0 ? 1.0f : j == 1 ? i10 : j == 2 ? i20 : i30;
+    dt[1] = j == 1 ? 1.0f : j == 2 ? i21 : j == 3 ? i31 : 0.0f;
+    dt[2] = j == 2 ? 1.0f : j == 3 ? i32 : 0.0f;
+    dt[3] = j == 3 ? 1.0f : 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float t = (r == c) ? 1.0f : 0.0f;
-#pragma unroll
-      for (int m = 0; m < r; ++m) t = fmaf(-ab[r * 16 + m], x[m], t);
-      x[r] = t;
+    for (int r = 0; r < 4; ++r) {
+      di[r] = dblk ? di[r] : 0.0f;
+      dt[r] = dblk ? dt[r] : 0.0f;
+      id[r] = dblk && j == r ? 1.0f : 0.0f;
+      lm[r] = lblk ? nd[r] : 0.0f;
     }
-    if (lg == 0) {
-      // stored as (I + A_bb)^{-1} diag(b) (column c scaled by b of token
-      // 16b + c); each value pinned in fp32 before its fp16 rounding, so no
-      // template instance fuses the scaling with the conversion
-      const float bc = sm.beta[HW][16 * WQ + c];
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const SplitF16 sl = split_f16(lm), sdt = split_f16(dt);
+    const f32x4 m = mfma_split(sdt, sl, z);    // M = (I + D)^{-1} L
+    const f32x4 mt = mfma_split(sl, sdt, z);   // M^T
+    const SplitF16 snm = split_f16(-m);
+    f32x4 x = id - mt;                         // I - Z
+    x = mfma_split(snm, split_f16(x), id);     // I - Z (I - Z)
+    x = mfma_split(snm, split_f16(x), id);     // (I + Z)^{-1}
+    // T^T = (I + D)^{-T} (I + M)^{-T}: lane (lr, lg) gets T[lr][4 lg + r],
+    // stored as (I + A_bb)^{-1} diag(b) (column 4 lg + r scaled by its b_t),
+    // each value pinned in fp32 before its fp16 rounding so no template
+    // instance fuses the scaling with the conversion
+    const f32x4 tt = mfma_split(split_f16(di), split_f16(x), z);
+    const f32x4 bc = *reinterpret_cast<const f32x4*>(&sm.beta[HW][16 * WQ + 4 * lg]);
+    f16x4 o;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float xr = x[r] * bc;
-        asm volatile("" : "+v"(xr));
-        sm.td[HW][WQ * 256 + r * 16 + c] = static_cast<_Float16>(xr);
-      }
+    for (int r = 0; r < 4; ++r) {
+      float v = tt[r] * bc[r];
+      asm volatile("" : "+v"(v));
+      o[r] = static_cast<_Float16>(v);
     }
+    *reinterpret_cast<f16x4*>(&sm.td[HW][WQ * 256 + lr * 16 + 4 * lg]) = o;
   }
 }
 
