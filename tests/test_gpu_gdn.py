@@ -225,6 +225,26 @@ def test_unnormalised_keys_bf16():
     check(c, TOL_BF16)
 
 
+@pytest.mark.parametrize("keys", ["identical", "near"])
+def test_repeated_keys_within_blocks(keys):
+    """Keys repeated (or nearly) over runs of 16 tokens with alpha = beta = 1:
+    the diagonal blocks of I + A are then all-ones lower triangles (or close
+    to them), the hardest case for the blocked inverse (its series terms are
+    largest there); the exact inverse is bidiagonal."""
+    from replay_inputs import to_bf16_bits
+    c = gdn_case([1000, 130, 63], 2, 4, 128, "bf16", seed=43, alpha="one", beta="one",
+                 normalize_q=True)
+    rng = np.random.default_rng(44)
+    T = int(c.cu_seqlens[-1])
+    base = rng.standard_normal((T // 16 + 1, c.h_k, 128))
+    kf = base[np.arange(T) // 16]
+    if keys == "near":
+        kf = kf + 0.05 * rng.standard_normal(kf.shape)
+    kf /= np.linalg.norm(kf, axis=-1, keepdims=True)
+    c.k = to_bf16_bits(kf)
+    check(c, TOL_BF16)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads in the launch configuration the benchmark times,
 # compared with the oracle on every sequence and head
