@@ -955,7 +955,6 @@ hipError_t launch4(const GdnArgs& a, hipStream_t s) {
 //    per wave, two waves per SIMD); the two-workgroup split measured slower
 //    here (8 x 32 chains, scalar decay: 168 against 146 us);
 //  * otherwise one head of 4 waves.
-constexpr int kGfx950Cus = 256;  // compute units of the gfx950 parts (MI350X, MI355X)
 template <int D, typename TI, typename TO>
 hipError_t launch3(const GdnArgs& a, hipStream_t s) {
   const int chains = a.n_seqs * a.h_v;

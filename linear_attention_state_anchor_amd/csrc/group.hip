@@ -220,6 +220,12 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, const floa
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, so each XCD is
 // given a contiguous range of a grouped order (8 M-tiles wide, walking N):
 // the ~32 tiles an XCD runs at a time share 8 A and 4 B panels in its L2.
+// Narrow variant (NJ = 1): the same tile split into four 256 x 64 strips, one
+// per workgroup (4 waves of 128 x 32), for the tiles of a last, partly
+// filled round: a launch of 260 tiles on 256 CUs would otherwise take two
+// full tile times.  Every output element is accumulated by the same MFMA
+// sequence over the same k order in both variants, so results do not depend
+// on which variant computed them.
 // Requirements: K % 64 == 0, N % 4 == 0, lda/ldb/ldc multiples of 8; M and
 // N are guarded.
 // ---------------------------------------------------------------------------
@@ -229,74 +235,101 @@ constexpr int EPI_SWIGLU = 2;
 constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8;
 constexpr int GGROUP = 8;  // M-tiles per group of the tile order
 constexpr int kXcdG = 8;   // XCDs
+constexpr int kStrips = 4; // 64-column strips per tile (narrow variant)
 
-template <int EPI>
+// Tile (tm, tn) at position q of the grouped order.
+__device__ __forceinline__ void gemm_tile_at(int q, int n_m, int n_n, int& tm, int& tn) {
+  const int group = q / (GGROUP * n_n), first = group * GGROUP;
+  const int gsz = min(n_m - first, GGROUP);
+  tm = first + (q % (GGROUP * n_n)) % gsz;
+  tn = (q % (GGROUP * n_n)) / gsz;
+}
+
+// Tiles q_begin .. q_begin + q_count - 1 of the grouped order: one per
+// workgroup (NJ = 4), or one 64-column strip per workgroup (NJ = 1).
+template <int EPI, int NJ>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict__ A, int lda,
                                                       const _Float16* __restrict__ Bt, int ldb,
-                                                      int M, int N, int K, void* C, int ldc) {
-  __shared__ _Float16 sm[2][2][GBM * GLD];  // [buffer][A | B]
-  constexpr int LOADS = GBM * GBK / 8 / 256;  // 16-byte loads per thread per operand
+                                                      int M, int N, int K, void* C, int ldc,
+                                                      int q_begin, int q_count) {
+  constexpr int BN = 64 * NJ;                 // columns of the workgroup
+  __shared__ _Float16 sm[2][GBM * GLD + BN * GLD];  // [buffer][A rows | B rows]
+  constexpr int LOADS = GBM * GBK / 8 / 256;  // 16-byte A loads per thread
+  constexpr int LOADB = BN * GBK / 8 / 256;   // 16-byte B loads per thread
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l = tid % kWave;
   const int wm = w / 2, wn = w % 2;
-  int tm, tn;
+  int tm, tn, strip = 0;
   {
     const int n_m = (M + GBM - 1) / GBM, n_n = (N + GBN - 1) / GBN;
-    const int tiles = n_m * n_n, per_xcd = (tiles + kXcdG - 1) / kXcdG;
-    const int q = (blockIdx.x % kXcdG) * per_xcd + blockIdx.x / kXcdG;
-    if (q >= tiles) return;
-    const int group = q / (GGROUP * n_n), first = group * GGROUP;
-    const int gsz = min(n_m - first, GGROUP);
-    tm = first + (q % (GGROUP * n_n)) % gsz;
-    tn = (q % (GGROUP * n_n)) / gsz;
+    int q;
+    if (NJ == 4) {
+      const int per_xcd = (q_count + kXcdG - 1) / kXcdG;
+      q = (blockIdx.x % kXcdG) * per_xcd + blockIdx.x / kXcdG;
+      if (q >= q_count) return;
+    } else {
+      q = blockIdx.x / kStrips;
+      strip = blockIdx.x % kStrips;
+      if (q >= q_count) return;
+    }
+    gemm_tile_at(q_begin + q, n_m, n_n, tm, tn);
   }
-  const int n0 = tn * GBN;
+  const int n0 = tn * GBN + BN * strip;
   const int m0 = tm * GBM;
+  if (n0 >= N) return;  // a strip past the last column
 
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  // Thread tid moves the 16-byte pieces (row tid/8 + 32e, chunk tid%8), e <
-  // LOADS, of each operand tile.  Rows past M (N) are clamped to the last
-  // row: they are computed and never stored, and the loop stays branch-free.
-  // Byte offsets fit in 32 bits (the launcher splits larger problems), so a
-  // load is one instruction: uniform base (k0) + per-thread offset.
-  uint32_t aoff[LOADS], boff[LOADS];
+  // Thread tid moves the 16-byte pieces (row tid/8 + 32e, chunk tid%8) of
+  // each operand tile.  Rows past M (N) are clamped to the last row: they
+  // are computed and never stored, and the loop stays branch-free.  Byte
+  // offsets fit in 32 bits (the launcher splits larger problems), so a load
+  // is one instruction: uniform base (k0) + per-thread offset.
+  uint32_t aoff[LOADS], boff[LOADB];
 #pragma unroll
   for (int e = 0; e < LOADS; ++e) {
     const int row = tid / (GBK / 8) + (256 / (GBK / 8)) * e, ch = tid % (GBK / 8);
     aoff[e] = static_cast<uint32_t>((static_cast<size_t>(min(m0 + row, M - 1)) * lda + 8 * ch) * 2);
+  }
+#pragma unroll
+  for (int e = 0; e < LOADB; ++e) {
+    const int row = tid / (GBK / 8) + (256 / (GBK / 8)) * e, ch = tid % (GBK / 8);
     boff[e] = static_cast<uint32_t>((static_cast<size_t>(min(n0 + row, N - 1)) * ldb + 8 * ch) * 2);
   }
-  u32x4 ra[LOADS], rb[LOADS];
+  u32x4 ra[LOADS], rb[LOADB];
   auto gload_a = [&](int k0, int e) {
     ra[e] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A + k0) + aoff[e]);
   };
   auto gload_b = [&](int k0, int e) {
     rb[e] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(Bt + k0) + boff[e]);
   };
-  auto store_tile = [&](int buf, int e) {
-    const int row = tid / (GBK / 8) + (256 / (GBK / 8)) * e, ch = tid % (GBK / 8);
-    *reinterpret_cast<u32x4*>(&sm[buf][0][row * GLD + 8 * ch]) = ra[e];
-    *reinterpret_cast<u32x4*>(&sm[buf][1][row * GLD + 8 * ch]) = rb[e];
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < LOADS; ++e) {
+      const int row = tid / (GBK / 8) + (256 / (GBK / 8)) * e, ch = tid % (GBK / 8);
+      *reinterpret_cast<u32x4*>(&sm[buf][row * GLD + 8 * ch]) = ra[e];
+      if (e < LOADB) *reinterpret_cast<u32x4*>(&sm[buf][GBM * GLD + row * GLD + 8 * ch]) = rb[e];
+    }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // lane l reads rows/columns l % 32 of each 32-wide fragment, k 8(l/32)..+7
-  f16x8 av[2][4], bv[2][4];
-  auto load_frag = [&](int buf, int ks, f16x8(&fa)[4], f16x8(&fb)[4]) {
+  f16x8 av[2][4], bv[2][NJ];
+  auto load_frag = [&](int buf, int ks, f16x8(&fa)[4], f16x8(&fb)[NJ]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      fa[i] = *reinterpret_cast<const f16x8*>(&sm[buf][0][(wm * 128 + 32 * i + l % 32) * GLD + 16 * ks + 8 * (l / 32)]);
+      fa[i] = *reinterpret_cast<const f16x8*>(&sm[buf][(wm * 128 + 32 * i + l % 32) * GLD + 16 * ks + 8 * (l / 32)]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[j] = *reinterpret_cast<const f16x8*>(&sm[buf][1][(wn * 128 + 32 * j + l % 32) * GLD + 16 * ks + 8 * (l / 32)]);
+    for (int j = 0; j < NJ; ++j)
+      fb[j] = *reinterpret_cast<const f16x8*>(
+          &sm[buf][GBM * GLD + (wn * 32 * NJ + 32 * j + l % 32) * GLD + 16 * ks + 8 * (l / 32)]);
   };
   // C^T tiles (B fragment as the first operand): a lane then holds 4
   // consecutive columns of one row, so the epilogue stores 4 values at once
@@ -304,22 +337,21 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(bv[h][j], av[h][i], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(bv[h][j], av[h][i], acc[i][j]);
   };
 
   const int nk = K / GBK;
 #pragma unroll
-  for (int e = 0; e < LOADS; ++e) {
-    gload_a(0, e);
-    gload_b(0, e);
-  }
+  for (int e = 0; e < LOADS; ++e) gload_a(0, e);
 #pragma unroll
-  for (int e = 0; e < LOADS; ++e) store_tile(0, e);
+  for (int e = 0; e < LOADB; ++e) gload_b(0, e);
+  store_tile(0);
   __syncthreads();
-  // Per k-tile: four k16 steps of 16 MFMAs.  Interleaved with them: the next
-  // step's fragment reads, the next k-tile's global loads (A in step 0, B in
-  // step 1) and its LDS stores (step 3, into the other buffer).  The last
-  // k-tile reloads itself, so the body has no branches.
+  // Per k-tile: four k16 steps of 4 NJ MFMAs per wave.  Interleaved with
+  // them (full tiles): the next step's fragment reads, the next k-tile's
+  // global loads (A in step 0, B in step 1) and its LDS stores (step 3, into
+  // the other buffer).  The last k-tile reloads itself, so the body has no
+  // branches.
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     const int kn = (kt + 1 < nk ? kt + 1 : kt) * GBK;
@@ -330,42 +362,49 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
 #pragma unroll
     for (int e = 0; e < LOADS; ++e) gload_a(kn, e);
     mma(0);
+    if constexpr (NJ == 4) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      for (int x = 0; x < 8; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // step 1
     load_frag(buf, 2, av[0], bv[0]);
 #pragma unroll
-    for (int e = 0; e < LOADS; ++e) gload_b(kn, e);
+    for (int e = 0; e < LOADB; ++e) gload_b(kn, e);
     mma(1);
+    if constexpr (NJ == 4) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      for (int x = 0; x < 8; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // step 2
     load_frag(buf, 3, av[1], bv[1]);
     mma(0);
+    if constexpr (NJ == 4) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      for (int x = 0; x < 8; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // step 3
-#pragma unroll
-    for (int e = 0; e < LOADS; ++e) store_tile(buf ^ 1, e);
+    store_tile(buf ^ 1);
     mma(1);
+    if constexpr (NJ == 4) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int x = 0; x < 16; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
@@ -377,10 +416,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
     const int m = m0 + wm * 128 + 32 * i + l % 32;
     if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 128 + 32 * j + 8 * g + 4 * (l / 32);
+        const int n = n0 + wn * 32 * NJ + 32 * j + 8 * g + 4 * (l / 32);
         if (n >= N) continue;  // N % 4 == 0: a group of 4 is in or out as a whole
         const size_t ci = static_cast<size_t>(m) * ldc + n;
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
@@ -648,14 +687,36 @@ hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, 
   for (int m_at = 0; m_at < M; m_at += mc) {
     const int mm = std::min(mc, M - m_at);
     const int tiles = ((N + GBN - 1) / GBN) * ((mm + GBM - 1) / GBM);
-    dim3 grid((tiles + kXcdG - 1) / kXcdG * kXcdG), block(256);
+    // Full rounds of whole tiles on the CUs; the tiles of a last, partly
+    // filled round go out as 64-column strips when their strips fit in one
+    // round: a strip does a quarter of a tile's MFMAs but still streams the
+    // whole A panel, and measures about half a tile's time (260 tiles of the
+    // 6552 x 2560 x 4096 output projection: 205 us as two rounds, 124 + 61 us
+    // with the last 4 tiles as 16 strips).
+    int full = tiles, narrow = 0;
+    const int rest = tiles % kGfx950Cus;
+    if (rest != 0 && kStrips * rest <= kGfx950Cus) {
+      full = tiles - rest;
+      narrow = rest;
+    }
     void* Cm = EPI == EPI_STORE32
                    ? static_cast<void*>(static_cast<float*>(C) + static_cast<size_t>(m_at) * ldc)
                    : static_cast<void*>(static_cast<_Float16*>(C) + static_cast<size_t>(m_at) * ldc);
-    hipLaunchKernelGGL((gemm_kernel<EPI>), grid, block, 0, s, A + static_cast<size_t>(m_at) * lda,
-                       lda, Bt, ldb, mm, N, K, Cm, ldc);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const _Float16* Am = A + static_cast<size_t>(m_at) * lda;
+    if (full > 0) {
+      dim3 grid((full + kXcdG - 1) / kXcdG * kXcdG), block(256);
+      hipLaunchKernelGGL((gemm_kernel<EPI, 4>), grid, block, 0, s, Am, lda, Bt, ldb, mm, N, K, Cm,
+                         ldc, 0, full);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (narrow > 0) {
+      dim3 grid(narrow * kStrips), block(256);
+      hipLaunchKernelGGL((gemm_kernel<EPI, 1>), grid, block, 0, s, Am, lda, Bt, ldb, mm, N, K, Cm,
+                         ldc, full, narrow);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

@@ -15,6 +15,7 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kGfx950Cus = 256;  // compute units of the gfx950 parts (MI350X, MI355X)
 
 // Element-type tags used as template parameters.
 struct BF16 {};
