@@ -437,33 +437,54 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// front end: one workgroup per 64-token block and head (grid y): causal
-// depthwise conv over the projection rows (zero history before each token's
-// sequence start) + SiLU on the k, v and q heads, per-head L2 norm of q and
-// k; the last y index does the gates of the block.  A wave walks 16 tokens
-// with a sliding window of the last `width` rows in registers; a lane owns
-// D/64 adjacent channels, so every row access is one coalesced 256-byte (or
-// 128-byte) wave load.  z is not copied: the gated RMSNorm reads it from P.
+// front end: one workgroup per 64-token block and 512 channels of one kind
+// (k, v or q heads; grid y): causal depthwise conv over the projection rows
+// (zero history before each token's sequence start, or the carried-in
+// window) + SiLU, per-head L2 norm of q and k; the last y index does the
+// gates of the block.  A wave walks 16 tokens with all the rows its window
+// needs loaded up front; a lane owns 8 adjacent channels (one 16-byte load
+// or store per row), so a head's 128 (64) channels sit in 16 (8) adjacent
+// lanes and its L2 sum is a DPP butterfly within them.  z is not copied:
+// the gated RMSNorm reads it from P.
 // ---------------------------------------------------------------------------
-constexpr int FT = 64;  // tokens per workgroup
+constexpr int FT = 64;    // tokens per workgroup
+constexpr int FCH = 512;  // channels per workgroup (8 per lane)
 
-// MAXW: conv widths up to MAXW (4 or 8); SiLU uses the hardware reciprocal
-// conv0 (may be null): per sequence the last width-1 pre-conv rows before
-// its first token ([n][conv_dim][width-1], original q|k|v channel order,
-// oldest first), used for the taps that reach before the sequence start
-// (continuation from a reconstructed state); null means zero history.
-template <int D, int MAXW>
+// Sum over the `n` (8 or 16) adjacent lanes of a head, in every such lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_all(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int LANES>
+__device__ __forceinline__ float head_sum(float x) {
+  x += dpp_all<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_all<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_all<0x141>(x);  // row_half_mirror: the other quad of the 8
+  if (LANES == 16) x += dpp_all<0x140>(x);  // row_mirror: the other 8 of the 16
+  return x;
+}
+
+// n_blocks: the y extent before the gate blocks, blocks per kind in
+// kb[0..2] (k, v, q); conv0 (may be null): per sequence the last width-1
+// pre-conv rows before its first token ([n][conv_dim][width-1], original
+// q|k|v channel order, oldest first), used for the taps that reach before
+// the sequence start (continuation from a reconstructed state); null means
+// zero history.  MAXW: conv widths up to MAXW (4 or 8).  HIST: conv0 may be
+// non-null (the replay path, without it, keeps a small fully unrolled body).
+template <int D, int MAXW, bool HIST>
 __global__ __launch_bounds__(256) void frontend_kernel(
     const _Float16* __restrict__ P, int ldp, LayerShape L, const float* __restrict__ convw,
     const int32_t* __restrict__ seq_start, const int32_t* __restrict__ seq_id,
-    const float* __restrict__ conv0, int T, float l2_eps, int n_conv_heads,
+    const float* __restrict__ conv0, int T, float l2_eps, int kb_k, int kb_v, int kb_q,
     _Float16* __restrict__ qo, _Float16* __restrict__ ko, _Float16* __restrict__ vo,
     float* __restrict__ la, float* __restrict__ be) {
-  constexpr int CPL = D / kWave;  // channels per lane
+  constexpr int CL = 8;                // channels per lane
+  constexpr int LPH = D / CL;          // lanes per head
+  constexpr int HPB = FCH / D;         // heads per workgroup
   const int t0 = blockIdx.x * FT;
-  const int hh = blockIdx.y;
+  const int by = blockIdx.y;
   const int nk = L.h_k, nv = L.h_v, W = L.width;
-  if (hh == n_conv_heads) {  // gates
+  if (by == kb_k + kb_v + kb_q) {  // gates
     for (int e = threadIdx.x; e < FT * nv; e += blockDim.x) {
       const int t = t0 + e / nv, h = e % nv;
       if (t >= T) break;
@@ -473,59 +494,64 @@ __global__ __launch_bounds__(256) void frontend_kernel(
     }
     return;
   }
-  int kind, hidx, pc0, nh, oc0;  // kind 0: k, 1: v, 2: q; oc0: original channel
+  // kind 0: k, 1: v, 2: q; pbase / obase: packed / original column of the
+  // kind's first channel
+  int kind, hb0, nh, pbase, obase;
   _Float16* out;
-  if (hh < nk) {
-    kind = 0; hidx = hh; pc0 = hh * D; nh = nk; out = ko; oc0 = (nk + hidx) * D;
-  } else if (hh < nk + nv) {
-    kind = 1; hidx = hh - nk; pc0 = nk * D + hidx * D; nh = nv; out = vo; oc0 = (2 * nk + hidx) * D;
+  if (by < kb_k) {
+    kind = 0; hb0 = by * HPB; nh = nk; pbase = 0; obase = nk * D; out = ko;
+  } else if (by < kb_k + kb_v) {
+    kind = 1; hb0 = (by - kb_k) * HPB; nh = nv; pbase = nk * D; obase = 2 * nk * D; out = vo;
   } else {
-    kind = 2; hidx = hh - nk - nv; pc0 = L.q_off() + hidx * D; nh = nk; out = qo; oc0 = hidx * D;
+    kind = 2; hb0 = (by - kb_k - kb_v) * HPB; nh = nk; pbase = L.q_off(); obase = 0; out = qo;
   }
   const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int c0 = CPL * lane;
-  const int ch0 = conv_channel(L, pc0 + c0);  // conv channels ch0 .. ch0+CPL-1
-  float wt[CPL][MAXW];  // wt[e][k]: tap applied to row t-k
+  const int hidx = hb0 + lane / LPH;          // this lane's head
+  const bool live = hidx < nh;
+  const int cin = CL * (lane % LPH);          // first channel within the head
+  const int pc = pbase + hidx * D + cin;      // packed column
+  const int ch0 = conv_channel(L, pc);        // conv channels ch0 .. ch0+7
+  const int oc = obase + hidx * D + cin;      // original q|k|v channel
+  float wt[CL][MAXW];  // wt[e][k]: tap applied to row t-k
 #pragma unroll
-  for (int e = 0; e < CPL; ++e)
+  for (int e = 0; e < CL; ++e)
 #pragma unroll
-    for (int k = 0; k < MAXW; ++k) wt[e][k] = k < W ? convw[(ch0 + e) * W + (W - 1 - k)] : 0.0f;
+    for (int k = 0; k < MAXW; ++k) wt[e][k] = live && k < W ? convw[(ch0 + e) * W + (W - 1 - k)] : 0.0f;
   // all input rows of this wave's 16 tokens are loaded up front (rows
   // tb-MAXW+1 .. tb+15; those before the window or outside [0, T) read 0)
   const int tb = t0 + 16 * wv;
   constexpr int NR = 16 + MAXW - 1;
-  typedef _Float16 h2 __attribute__((ext_vector_type(CPL)));
-  h2 u[NR];
+  f16x8 u[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int row = tb - (MAXW - 1) + r;
-    const bool ok = row >= 0 && row < T && r >= MAXW - W;
-    u[r] = ok ? *reinterpret_cast<const h2*>(P + static_cast<size_t>(row) * ldp + pc0 + c0) : h2{};
+    const bool ok = live && row >= 0 && row < T && r >= MAXW - W;
+    u[r] = ok ? *reinterpret_cast<const f16x8*>(P + static_cast<size_t>(row) * ldp + pc) : f16x8{};
   }
   // sequence starts (and ids) of the wave's 16 tokens, one per lane
   // (broadcast below)
   const int sq = seq_start[min(tb + lane % 16, T - 1)];
-  const int sid = conv0 ? seq_id[min(tb + lane % 16, T - 1)] : 0;
+  const int sid = HIST && conv0 ? seq_id[min(tb + lane % 16, T - 1)] : 0;
   const int W1 = W - 1;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int t = tb + i;
     const int back = t < T ? t - __builtin_amdgcn_readlane(sq, i) : -1;  // rows t-back .. t: t's sequence
-    float y[CPL];
+    float y[CL];
     float ss = 0.0f;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
+    for (int e = 0; e < CL; ++e) {
       float acc = 0.0f;
 #pragma unroll
       for (int k = 0; k < MAXW; ++k) {  // row t-k is u[MAXW-1+i-k]
         if (k <= back) {
           acc = fmaf(wt[e][k], static_cast<float>(u[MAXW - 1 + i - k][e]), acc);
-        } else if (conv0 && k < W && back >= 0) {
+        } else if (HIST && conv0 && k < W && back >= 0 && live) {
           // row t-k lies k-back rows before the sequence start: entry
           // W-1-(k-back) of the carried-in window
           const int n = __builtin_amdgcn_readlane(sid, i);
           acc = fmaf(wt[e][k],
-                     conv0[(static_cast<size_t>(n) * L.conv_dim() + oc0 + c0 + e) * W1 + (W1 - (k - back))],
+                     conv0[(static_cast<size_t>(n) * L.conv_dim() + oc + e) * W1 + (W1 - (k - back))],
                      acc);
         }
       }
@@ -533,15 +559,15 @@ __global__ __launch_bounds__(256) void frontend_kernel(
       ss = fmaf(y[e], y[e], ss);
     }
     if (kind != 1) {
-      const float inv = rsqrtf(wave_sum(ss) + l2_eps);
+      const float inv = rsqrtf(head_sum<LPH>(ss) + l2_eps);
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) y[e] *= inv;
+      for (int e = 0; e < CL; ++e) y[e] *= inv;
     }
-    if (t < T) {
-      h2 o;
+    if (t < T && live) {
+      f16x8 o;
 #pragma unroll
-      for (int e = 0; e < CPL; ++e) o[e] = static_cast<_Float16>(y[e]);
-      *reinterpret_cast<h2*>(out + (static_cast<size_t>(t) * nh + hidx) * D + c0) = o;
+      for (int e = 0; e < CL; ++e) o[e] = static_cast<_Float16>(y[e]);
+      *reinterpret_cast<f16x8*>(out + (static_cast<size_t>(t) * nh + hidx) * D + cin) = o;
     }
   }
 }
@@ -895,12 +921,20 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
                                     s) != hipSuccess)
         return SR_ELAUNCH;
       // conv heads: k, v (and q unless this is the last layer), then gates
-      const int n_conv = full ? 2 * d->h_k + d->h_v : d->h_k + d->h_v;
-      const dim3 fgrid((T + sr::FT - 1) / sr::FT, n_conv + 1);
-      auto fe = d->d == 128 ? (L.width <= 4 ? sr::frontend_kernel<128, 4> : sr::frontend_kernel<128, 8>)
-                            : (L.width <= 4 ? sr::frontend_kernel<64, 4> : sr::frontend_kernel<64, 8>);
+      const int hpb = sr::FCH / d->d;  // heads per front-end workgroup
+      const int kb_k = (d->h_k + hpb - 1) / hpb, kb_v = (d->h_v + hpb - 1) / hpb;
+      const int kb_q = full ? kb_k : 0;
+      const dim3 fgrid((T + sr::FT - 1) / sr::FT, kb_k + kb_v + kb_q + 1);
+      auto fe = lconv0 ? (d->d == 128 ? (L.width <= 4 ? sr::frontend_kernel<128, 4, true>
+                                                      : sr::frontend_kernel<128, 8, true>)
+                                      : (L.width <= 4 ? sr::frontend_kernel<64, 4, true>
+                                                      : sr::frontend_kernel<64, 8, true>))
+                       : (d->d == 128 ? (L.width <= 4 ? sr::frontend_kernel<128, 4, false>
+                                                      : sr::frontend_kernel<128, 8, false>)
+                                      : (L.width <= 4 ? sr::frontend_kernel<64, 4, false>
+                                                      : sr::frontend_kernel<64, 8, false>));
       hipLaunchKernelGGL(fe, fgrid, dim3(256), 0, s, P, L.n_all(), L, convw, sst, sid, lconv0, T,
-                         d->l2_eps, n_conv, qb, kb, vb, la, be);
+                         d->l2_eps, kb_k, kb_v, kb_q, qb, kb, vb, la, be);
       if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
       if (conv_states) {
         hipLaunchKernelGGL(sr::conv_state_kernel, dim3(64, d->n_seqs), dim3(256), 0, s, P, L.n_all(),
