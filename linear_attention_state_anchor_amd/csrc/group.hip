@@ -8,6 +8,9 @@
 //   P    = xh W_in (fp16), packed columns k|v|a|b|pad|q|z  gemm_kernel (MFMA)
 //   q,k  = L2norm(SiLU(conv(P_q,P_k))), v = SiLU(conv(P_v)),
 //   log a = -softplus(P_a), b = sigmoid(P_b)               frontend_kernel
+//   (for conv widths up to 4 with zero history the projection and the conv,
+//   SiLU and L2 norms are one kernel, gemm_front_kernel, and P keeps only
+//   z and a|b; gates_kernel forms the gates)
 //   S, o = gated delta rule from S_0 = 0                   launch_gdn_chunk
 //   y    = rms(o) o SiLU(P_z) per value head               gated_norm_kernel
 //   D    = y W_out (fp32); x <- x + D in the next RMSNorm   gemm_kernel (MFMA)
@@ -245,43 +248,29 @@ __device__ __forceinline__ void gemm_tile_at(int q, int n_m, int n_n, int& tm, i
   tn = (q % (GGROUP * n_n)) / gsz;
 }
 
-// Tiles q_begin .. q_begin + q_count - 1 of the grouped order: one per
-// workgroup (NJ = 4), or one 64-column strip per workgroup (NJ = 1).
-template <int EPI, int NJ>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict__ A, int lda,
-                                                      const _Float16* __restrict__ Bt, int ldb,
-                                                      int M, int N, int K, void* C, int ldc,
-                                                      int q_begin, int q_count) {
+// Main loop of one tile: rows m0 .. m0+255 of A (clamped into [0, M)),
+// columns n0 .. n0+64NJ-1 of Bt (clamped below N), all of K.  sm: the
+// kernel's LDS, [2][GBM*GLD + 64NJ*GLD] halves.  On return acc holds C^T
+// fragments: lane l has row m0 + wm*128 + 32i + l%32 and, in register group
+// g = r/4, columns n0 + wn*32NJ + 32j + 8g + 4(l/32) .. +3.
+template <int NJ>
+__device__ __forceinline__ void gemm_mainloop(const _Float16* __restrict__ A, int lda,
+                                              const _Float16* __restrict__ Bt, int ldb, int M,
+                                              int N, int K, int m0, int n0, _Float16* sm_,
+                                              f32x16 (&acc)[4][NJ]) {
   constexpr int BN = 64 * NJ;                 // columns of the workgroup
-  __shared__ _Float16 sm[2][GBM * GLD + BN * GLD];  // [buffer][A rows | B rows]
+  constexpr int SB = GBM * GLD + BN * GLD;    // halves per buffer
   constexpr int LOADS = GBM * GBK / 8 / 256;  // 16-byte A loads per thread
   constexpr int LOADB = BN * GBK / 8 / 256;   // 16-byte B loads per thread
+  _Float16 (*sm)[SB] = reinterpret_cast<_Float16 (*)[SB]>(sm_);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l = tid % kWave;
   const int wm = w / 2, wn = w % 2;
-  int tm, tn, strip = 0;
-  {
-    const int n_m = (M + GBM - 1) / GBM, n_n = (N + GBN - 1) / GBN;
-    int q;
-    if (NJ == 4) {
-      const int per_xcd = (q_count + kXcdG - 1) / kXcdG;
-      q = (blockIdx.x % kXcdG) * per_xcd + blockIdx.x / kXcdG;
-      if (q >= q_count) return;
-    } else {
-      q = blockIdx.x / kStrips;
-      strip = blockIdx.x % kStrips;
-      if (q >= q_count) return;
-    }
-    gemm_tile_at(q_begin + q, n_m, n_n, tm, tn);
-  }
-  const int n0 = tn * GBN + BN * strip;
-  const int m0 = tm * GBM;
-  if (n0 >= N) return;  // a strip past the last column
 
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   // Thread tid moves the 16-byte pieces (row tid/8 + 32e, chunk tid%8) of
-  // each operand tile.  Rows past M (N) are clamped to the last row: they
+  // each operand tile.  Rows outside [0, M) (N) are clamped into range: they
   // are computed and never stored, and the loop stays branch-free.  Byte
   // offsets fit in 32 bits (the launcher splits larger problems), so a load
   // is one instruction: uniform base (k0) + per-thread offset.
@@ -289,7 +278,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
 #pragma unroll
   for (int e = 0; e < LOADS; ++e) {
     const int row = tid / (GBK / 8) + (256 / (GBK / 8)) * e, ch = tid % (GBK / 8);
-    aoff[e] = static_cast<uint32_t>((static_cast<size_t>(min(m0 + row, M - 1)) * lda + 8 * ch) * 2);
+    aoff[e] = static_cast<uint32_t>(
+        (static_cast<size_t>(min(max(m0 + row, 0), M - 1)) * lda + 8 * ch) * 2);
   }
 #pragma unroll
   for (int e = 0; e < LOADB; ++e) {
@@ -312,7 +302,6 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
     }
   };
 
-  f32x16 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -409,6 +398,41 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
+}
+
+// Tiles q_begin .. q_begin + q_count - 1 of the grouped order: one per
+// workgroup (NJ = 4), or one 64-column strip per workgroup (NJ = 1).
+template <int EPI, int NJ>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict__ A, int lda,
+                                                      const _Float16* __restrict__ Bt, int ldb,
+                                                      int M, int N, int K, void* C, int ldc,
+                                                      int q_begin, int q_count) {
+  constexpr int BN = 64 * NJ;                 // columns of the workgroup
+  __shared__ _Float16 sm[2 * (GBM * GLD + BN * GLD)];  // [buffer][A rows | B rows]
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l = tid % kWave;
+  const int wm = w / 2, wn = w % 2;
+  int tm, tn, strip = 0;
+  {
+    const int n_m = (M + GBM - 1) / GBM, n_n = (N + GBN - 1) / GBN;
+    int q;
+    if (NJ == 4) {
+      const int per_xcd = (q_count + kXcdG - 1) / kXcdG;
+      q = (blockIdx.x % kXcdG) * per_xcd + blockIdx.x / kXcdG;
+      if (q >= q_count) return;
+    } else {
+      q = blockIdx.x / kStrips;
+      strip = blockIdx.x % kStrips;
+      if (q >= q_count) return;
+    }
+    gemm_tile_at(q_begin + q, n_m, n_n, tm, tn);
+  }
+  const int n0 = tn * GBN + BN * strip;
+  const int m0 = tm * GBM;
+  if (n0 >= N) return;  // a strip past the last column
+  f32x16 acc[4][NJ];
+  gemm_mainloop<NJ>(A, lda, Bt, ldb, M, N, K, m0, n0, sm, acc);
   // epilogue: lane holds row m = l%32 of fragment i and, in register group
   // g = r/4, columns 8g + 4(l/32) .. +3 of fragment j
 #pragma unroll
@@ -544,16 +568,16 @@ __global__ __launch_bounds__(256) void frontend_kernel(
       float acc = 0.0f;
 #pragma unroll
       for (int k = 0; k < MAXW; ++k) {  // row t-k is u[MAXW-1+i-k]
-        if (k <= back) {
-          acc = fmaf(wt[e][k], static_cast<float>(u[MAXW - 1 + i - k][e]), acc);
-        } else if (HIST && conv0 && k < W && back >= 0 && live) {
+        // taps before the sequence start see zero (or the carried window);
+        // selected rather than branched on, so the body stays branch-free
+        float x = k <= back ? static_cast<float>(u[MAXW - 1 + i - k][e]) : 0.0f;
+        if (HIST && k > back && conv0 && k < W && back >= 0 && live) {
           // row t-k lies k-back rows before the sequence start: entry
           // W-1-(k-back) of the carried-in window
           const int n = __builtin_amdgcn_readlane(sid, i);
-          acc = fmaf(wt[e][k],
-                     conv0[(static_cast<size_t>(n) * L.conv_dim() + oc + e) * W1 + (W1 - (k - back))],
-                     acc);
+          x = conv0[(static_cast<size_t>(n) * L.conv_dim() + oc + e) * W1 + (W1 - (k - back))];
         }
+        acc = fmaf(wt[e][k], x, acc);
       }
       y[e] = acc * __builtin_amdgcn_rcpf(1.0f + __expf(-acc));  // SiLU
       ss = fmaf(y[e], y[e], ss);
@@ -570,6 +594,155 @@ __global__ __launch_bounds__(256) void frontend_kernel(
       *reinterpret_cast<f16x8*>(out + (static_cast<size_t>(t) * nh + hidx) * D + cin) = o;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Input projection fused with the front end (conv widths up to 4 with zero
+// history): the same main loop as gemm_kernel, then the tile goes through
+// LDS in fp16 (the values the separate front end would read from P) and the
+// front end runs on it, so the conv channels of P never reach HBM; z is
+// stored to P for the gated RMSNorm, a and b become the gates.  M tiles
+// overlap by 3 rows: tile tm computes rows 253 tm - 3 .. 253 tm + 252 and
+// emits the last 253, so every emitted row has its three conv predecessors
+// in the tile.  Every value is computed exactly as gemm_kernel<EPI_STORE16>
+// followed by frontend_kernel computes it (same fp16 rounding, tap order,
+// SiLU and L2 sum).  A lane owns 8 adjacent columns of the tile and walks 32
+// rows, four at a time.  The a|b columns go to P like z; gates_kernel
+// forms the gates from them.
+// ---------------------------------------------------------------------------
+constexpr int FTM = GBM - 3;   // rows emitted per tile
+constexpr int FTS = GBN + 8;   // row stride (halves) of the staged tile
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void gemm_front_kernel(
+    const _Float16* __restrict__ A, int lda, const _Float16* __restrict__ Bt, int ldb, int M,
+    int N, int K, LayerShape L, const float* __restrict__ convw,
+    const int32_t* __restrict__ seq_start, float l2_eps, _Float16* __restrict__ P, int ldp,
+    _Float16* __restrict__ qo, _Float16* __restrict__ ko, _Float16* __restrict__ vo) {
+  __shared__ _Float16 sm[2 * (GBM * GLD + GBN * GLD)];
+  __shared__ int sst[GBM];
+  static_assert(GBM * FTS <= 2 * (GBM * GLD + GBN * GLD), "staged tile must fit the LDS buffers");
+  constexpr int LPH = D / 8;  // lanes per head
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l = tid % kWave;
+  const int wm = w / 2, wn = w % 2;
+  int tm, tn;
+  {
+    const int n_m = (M + FTM - 1) / FTM, n_n = (N + GBN - 1) / GBN;
+    const int tiles = n_m * n_n, per_xcd = (tiles + kXcdG - 1) / kXcdG;
+    const int q = (blockIdx.x % kXcdG) * per_xcd + blockIdx.x / kXcdG;
+    if (q >= tiles) return;
+    gemm_tile_at(q, n_m, n_n, tm, tn);
+  }
+  const int n0 = tn * GBN;
+  const int m0 = tm * FTM - 3;
+  f32x16 acc[4][4];
+  gemm_mainloop<4>(A, lda, Bt, ldb, M, N, K, m0, n0, sm, acc);
+  // (the main loop ends with a barrier: its LDS buffers are free)
+  {
+    const int t = m0 + tid;
+    sst[tid] = t >= 0 && t < M ? seq_start[t] : 0;
+  }
+  _Float16* const T16 = sm;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = wm * 128 + 32 * i + l % 32;
+        const int col = wn * 128 + 32 * j + 8 * g + 4 * (l / 32);
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        *reinterpret_cast<f16x4*>(T16 + row * FTS + col) = to_f16x4(v);
+      }
+  __syncthreads();
+
+  // this lane's 8 columns and what they are
+  const int cb = l % 32;
+  const int col = n0 + 8 * cb;
+  const int hk = L.h_k, hv = L.h_v;
+  int kind = -1, hidx = 0, nh = 1, cin = 0;  // 0 k, 1 v, 2 q, 3 gates, 4 z
+  _Float16* out = nullptr;
+  if (col < N) {
+    if (col < hk * D) {
+      kind = 0; hidx = col / D; nh = hk; out = ko; cin = col % D;
+    } else if (col < L.n_kv()) {
+      kind = 1; hidx = (col - hk * D) / D; nh = hv; out = vo; cin = (col - hk * D) % D;
+    } else if (col < L.n_state()) {
+      kind = 3;
+    } else if (col >= L.q_off() && col < L.q_off() + hk * D) {
+      kind = 2; hidx = (col - L.q_off()) / D; nh = hk; out = qo; cin = (col - L.q_off()) % D;
+    } else if (col >= L.z_off() && col < L.z_off() + hv * D) {
+      kind = 4;
+    }
+  }
+  const bool conv = kind >= 0 && kind <= 2;
+  const int ch0 = conv ? conv_channel(L, col) : 0;
+  const int W = L.width;
+  float wt[8][4];  // wt[e][k]: tap applied to row t-k
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wt[e][k] = conv && k < W ? convw[(ch0 + e) * W + (W - 1 - k)] : 0.0f;
+
+  // rows r0 .. r1-1, four at a time (independent rows: their loads, conv,
+  // SiLU and L2 sums overlap); u[j] holds row rb - 3 + j
+  const int r0 = 3 + 32 * (w * 2 + l / 32), r1 = min(r0 + 32, GBM);
+  f16x8 u[7];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) u[j] = *reinterpret_cast<const f16x8*>(T16 + (r0 - 3 + j) * FTS + 8 * cb);
+  for (int rb = r0; rb < r1; rb += 4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      u[3 + q] = *reinterpret_cast<const f16x8*>(T16 + min(rb + q, GBM - 1) * FTS + 8 * cb);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = rb + q;
+      const int t = m0 + r;
+      const bool emit = r < r1 && t < M;  // uniform within each 32-lane half
+      const int back = t - sst[min(r, GBM - 1)];  // rows t-back .. t belong to t's sequence
+      float y[8];
+      float ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)  // row t-k is u[3 + q - k]
+          a = fmaf(wt[e][k], k <= back ? static_cast<float>(u[3 + q - k][e]) : 0.0f, a);
+        y[e] = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));  // SiLU
+        ss = fmaf(y[e], y[e], ss);
+      }
+      const float inv = rsqrtf(head_sum<LPH>(ss) + l2_eps);  // every lane of the head takes part
+      if (!emit) continue;
+      if (conv) {
+        f16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = static_cast<_Float16>(kind != 1 ? y[e] * inv : y[e]);
+        *reinterpret_cast<f16x8*>(out + (static_cast<size_t>(t) * nh + hidx) * D + cin) = o;
+      } else if (kind >= 3) {
+        // z, and the raw a|b columns (gates_kernel turns them into the gates:
+        // the 8 lanes that hold them would otherwise hold up the tile)
+        *reinterpret_cast<f16x8*>(P + static_cast<size_t>(t) * ldp + col) = u[3 + q];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) u[j] = u[4 + j];
+  }
+}
+
+// Gates from the raw a|b projection columns: log a = -softplus(P_a),
+// b = sigmoid(P_b), one thread per (token, value head).
+__global__ __launch_bounds__(256) void gates_kernel(const _Float16* __restrict__ P, int ldp,
+                                                    LayerShape L, int T, float* __restrict__ la,
+                                                    float* __restrict__ be) {
+  const size_t e = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  const int nv = L.h_v;
+  if (e >= static_cast<size_t>(T) * nv) return;
+  const size_t t = e / nv;
+  const int h = static_cast<int>(e % nv);
+  la[e] = -softplus(static_cast<float>(P[t * ldp + L.a_off() + h]));
+  be[e] = sigmoid(static_cast<float>(P[t * ldp + L.b_off() + h]));
 }
 
 // conv state: last W-1 pre-conv rows of q|k|v per sequence (original
@@ -917,6 +1090,28 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
       const int N = full ? L.n_all()
                   : conv_states ? static_cast<int>(sr::align_up(L.q_off() + d->h_k * d->d, 128))
                                 : L.n_state_pad();
+      // Projection and front end in one kernel unless the conv needs a
+      // carried window (extension), a width above 4, or P's conv columns
+      // (the conv windows are returned), or A is too large for 32-bit offsets
+      const bool fuse = L.width <= 4 && !lconv0 && !conv_states &&
+                        static_cast<size_t>(T) * d->hidden * 2 < (size_t{1} << 31);
+      if (fuse) {
+        const int n_m = (T + sr::FTM - 1) / sr::FTM, n_n = (N + sr::GBN - 1) / sr::GBN;
+        const dim3 grid((n_m * n_n + sr::kXcdG - 1) / sr::kXcdG * sr::kXcdG);
+        if (d->d == 128)
+          hipLaunchKernelGGL(sr::gemm_front_kernel<128>, grid, dim3(256), 0, s, xh, d->hidden, win,
+                             d->hidden, T, N, d->hidden, L, convw, sst, d->l2_eps, P, L.n_all(),
+                             qb, kb, vb);
+        else
+          hipLaunchKernelGGL(sr::gemm_front_kernel<64>, grid, dim3(256), 0, s, xh, d->hidden, win,
+                             d->hidden, T, N, d->hidden, L, convw, sst, d->l2_eps, P, L.n_all(),
+                             qb, kb, vb);
+        if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+        const size_t ng = static_cast<size_t>(T) * d->h_v;
+        hipLaunchKernelGGL(sr::gates_kernel, dim3(static_cast<unsigned>((ng + 255) / 256)), dim3(256),
+                           0, s, P, L.n_all(), L, T, la, be);
+        if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+      } else {
       if (sr::gemm<sr::EPI_STORE16>(xh, d->hidden, win, d->hidden, T, N, d->hidden, P, L.n_all(),
                                     s) != hipSuccess)
         return SR_ELAUNCH;
@@ -936,6 +1131,7 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
       hipLaunchKernelGGL(fe, fgrid, dim3(256), 0, s, P, L.n_all(), L, convw, sst, sid, lconv0, T,
                          d->l2_eps, kb_k, kb_v, kb_q, qb, kb, vb, la, be);
       if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+      }
       if (conv_states) {
         hipLaunchKernelGGL(sr::conv_state_kernel, dim3(64, d->n_seqs), dim3(256), 0, s, P, L.n_all(),
                            L, cu_seqlens, d->n_seqs, lconv0, conv_states + conv_stride * li);

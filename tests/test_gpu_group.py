@@ -52,8 +52,15 @@ def gpu_group(g, anchors_dev=None, cu_dev=None, packed=None):
     states, conv = sr.replay_group(anchors_dev, packed, cu_dev, g.layer_kind, g.h_k, g.h_v,
                                    g.d, conv_width=g.conv_width, want_conv_state=True,
                                    ffn_dim=ffn_dim(g))
+    # without the conv windows the projection and the front end run as one
+    # kernel (widths up to 4); every value must come out identical
+    states_f = sr.replay_group(anchors_dev, packed, cu_dev, g.layer_kind, g.h_k, g.h_v,
+                               g.d, conv_width=g.conv_width, want_conv_state=False,
+                               ffn_dim=ffn_dim(g))
     torch.cuda.synchronize()
-    return to_np(states), to_np(conv)
+    states, states_f = to_np(states), to_np(states_f)
+    np.testing.assert_array_equal(states_f, states)
+    return states, to_np(conv)
 
 
 def oracle_group(g, anchors=None, cu=None):
