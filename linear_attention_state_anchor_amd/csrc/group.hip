@@ -330,6 +330,53 @@ __device__ __forceinline__ void gemm_mainloop(const _Float16* __restrict__ A, in
   };
 
   const int nk = K / GBK;
+  if constexpr (NJ == 1) {
+    // Strips do a quarter of a tile's MFMAs per k-tile, too few to cover a
+    // k-tile of load latency: their loads run two k-tiles ahead, in two
+    // register stages (k-tile kt+1 is stored to LDS at the end of k-tile kt,
+    // k-tile kt+2 is issued at its start).  Same k order as the tiles.
+    u32x4 ra2[LOADS], rb2[LOADB];
+    auto issue = [&](u32x4(&xa)[LOADS], u32x4(&xb)[LOADB], int kt) {
+      const int k0 = min(kt, nk - 1) * GBK;
+#pragma unroll
+      for (int e = 0; e < LOADS; ++e)
+        xa[e] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(A + k0) + aoff[e]);
+#pragma unroll
+      for (int e = 0; e < LOADB; ++e)
+        xb[e] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(Bt + k0) + boff[e]);
+    };
+    auto stash = [&](const u32x4(&xa)[LOADS], const u32x4(&xb)[LOADB], int buf) {
+#pragma unroll
+      for (int e = 0; e < LOADS; ++e) {
+        const int row = tid / (GBK / 8) + (256 / (GBK / 8)) * e, ch = tid % (GBK / 8);
+        *reinterpret_cast<u32x4*>(&sm[buf][row * GLD + 8 * ch]) = xa[e];
+        if (e < LOADB) *reinterpret_cast<u32x4*>(&sm[buf][GBM * GLD + row * GLD + 8 * ch]) = xb[e];
+      }
+    };
+    auto step = [&](int buf) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        load_frag(buf, ks, av[0], bv[0]);
+        mma(0);
+      }
+    };
+    issue(ra, rb, 0);
+    stash(ra, rb, 0);
+    issue(ra, rb, 1);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      issue(ra2, rb2, kt + 2);
+      step(0);
+      stash(ra, rb, 1);  // k-tile kt + 1
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      issue(ra, rb, kt + 3);
+      step(1);
+      stash(ra2, rb2, 0);  // k-tile kt + 2
+      __syncthreads();
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < LOADS; ++e) gload_a(0, e);
 #pragma unroll
