@@ -95,6 +95,19 @@ def test_small_group(kinds):
     check(g)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_sequence_starts_at_projection_tile_edges(d):
+    """Sequences that start right at, and just after, the rows where the
+    fused projection's overlapping M tiles meet (every 253 rows: each tile
+    recomputes the 3 rows before its first emitted row), very short
+    sequences, and a total that leaves a last tile of a few rows.  gpu_group
+    asserts the fused and separate front ends agree bit for bit; the oracle
+    checks the values."""
+    lens = [253, 1, 2, 3, 247, 253, 255, 1, 40]   # starts at 253, 254, 256, 259, 506, ...
+    g = _group(lens, 31, 256, 2, 4, d, [GDN, GDN, FA])
+    check(g)
+
+
 @pytest.mark.parametrize("width", [2, 6, 8])
 def test_conv_widths(width):
     """Conv widths other than 4 (the wider ones take the 8-tap front end)."""
