@@ -733,16 +733,34 @@ __global__ __launch_bounds__(256, 1) void gemm_front_kernel(
 #pragma unroll
     for (int k = 0; k < 4; ++k) wt[e][k] = conv && k < W ? convw[(ch0 + e) * W + (W - 1 - k)] : 0.0f;
 
-  // rows r0 .. r1-1, four at a time (independent rows: their loads, conv,
-  // SiLU and L2 sums overlap); u[j] holds row rb - 3 + j
   const int r0 = 3 + 32 * (w * 2 + l / 32), r1 = min(r0 + 32, GBM);
+  // tiles without conv columns (z, pad) only copy z (and a|b) to P
+  const bool any_conv = n0 < L.n_kv() || (n0 < L.q_off() + hk * D && n0 + GBN > L.q_off());
+  if (!any_conv) {
+    if (kind >= 3)
+      for (int r = r0; r < r1 && m0 + r < M; ++r)
+        *reinterpret_cast<f16x8*>(P + static_cast<size_t>(m0 + r) * ldp + col) =
+            *reinterpret_cast<const f16x8*>(T16 + r * FTS + 8 * cb);
+    return;
+  }
+  // rows r0 .. r1-1, four at a time (independent rows: their loads, conv,
+  // SiLU and L2 sums overlap); u[j] / uf[j] hold row rb - 3 + j in fp16 (as
+  // staged) and fp32 (each value converted once)
   f16x8 u[7];
+  float uf[7][8];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) u[j] = *reinterpret_cast<const f16x8*>(T16 + (r0 - 3 + j) * FTS + 8 * cb);
+  for (int j = 0; j < 3; ++j) {
+    u[j] = *reinterpret_cast<const f16x8*>(T16 + (r0 - 3 + j) * FTS + 8 * cb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) uf[j][e] = static_cast<float>(u[j][e]);
+  }
   for (int rb = r0; rb < r1; rb += 4) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 4; ++q) {
       u[3 + q] = *reinterpret_cast<const f16x8*>(T16 + min(rb + q, GBM - 1) * FTS + 8 * cb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) uf[3 + q][e] = static_cast<float>(u[3 + q][e]);
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = rb + q;
@@ -751,14 +769,24 @@ __global__ __launch_bounds__(256, 1) void gemm_front_kernel(
       const int back = t - sst[min(r, GBM - 1)];  // rows t-back .. t belong to t's sequence
       float y[8];
       float ss = 0.0f;
+      if (back >= 3) {  // every tap inside the sequence (the common case)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float a = 0.0f;
+        for (int e = 0; e < 8; ++e) {
+          float a = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)  // row t-k is u[3 + q - k]
-          a = fmaf(wt[e][k], k <= back ? static_cast<float>(u[3 + q - k][e]) : 0.0f, a);
-        y[e] = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));  // SiLU
-        ss = fmaf(y[e], y[e], ss);
+          for (int k = 0; k < 4; ++k) a = fmaf(wt[e][k], uf[3 + q - k][e], a);
+          y[e] = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));  // SiLU
+          ss = fmaf(y[e], y[e], ss);
+        }
+      } else {  // taps before the sequence start see zero
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float a = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) a = fmaf(wt[e][k], k <= back ? uf[3 + q - k][e] : 0.0f, a);
+          y[e] = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+          ss = fmaf(y[e], y[e], ss);
+        }
       }
       const float inv = rsqrtf(head_sum<LPH>(ss) + l2_eps);  // every lane of the head takes part
       if (!emit) continue;
@@ -774,7 +802,11 @@ __global__ __launch_bounds__(256, 1) void gemm_front_kernel(
       }
     }
 #pragma unroll
-    for (int j = 0; j < 3; ++j) u[j] = u[4 + j];
+    for (int j = 0; j < 3; ++j) {
+      u[j] = u[4 + j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) uf[j][e] = uf[4 + j][e];
+    }
   }
 }
 
