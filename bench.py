@@ -193,6 +193,29 @@ def time_steps(fn, steps, warmup):
             "p10_ms": pct(0.1), "p90_ms": pct(0.9), "min_ms": per[0], "max_ms": per[-1]}
 
 
+def time_cold(fn, reps=20, scrub_mib=512):
+    """Median time of fn with a 512 MiB write between calls, which evicts
+    the 256 MB infinity cache (MALL) and the L2s, so the call reads its
+    inputs from HBM: the cold counterpart of time_steps' warm figure.  Only
+    the call is inside the events."""
+    import torch
+    scrub = torch.empty((scrub_mib << 20,), dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    per = []
+    for i in range(reps):
+        scrub.fill_(i & 255)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    del scrub
+    per.sort()
+    return per[len(per) // 2]
+
+
 def replay_entry(t, T, byts, flops):
     ms = t["mean_ms"]
     sec = ms / 1e3
@@ -232,6 +255,9 @@ def bench_replay_variants(steps, warmup, to_dev, q, k, v, alpha, beta, cu, S):
     out["erase_free"] = dict(workload="erase-free (scalar decay) replay, 8 x 2048, 32 heads, "
                                       "d=128, bf16 in/out, beta = 1",
                              **replay_entry(t, c.total_tokens, byts, flops))
+    out["erase_free"]["cold_median_ms"] = time_cold(
+        lambda: sr.gdn_replay_state(q2, k2, v2, a2, None, cu2, None, erase=False,
+                                    alpha_is_log=c.alpha_is_log, final_state=S2, o=o2))
     return out
 
 
@@ -392,6 +418,9 @@ def bench_continuation_and_handoff(steps, warmup, to_dev):
         "tokens_per_s": 64 / (t["mean_ms"] / 1e3),
         "hbm_gbs": byts / (t["mean_ms"] / 1e3) / 1e9,
         "hbm_frac": byts / (t["mean_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": byts}
+    tc = time_cold(lambda: sr.gdn_decode_step(q, k, v, a, b, S, alpha_is_log=True, o=o))
+    out["decode_step"].update({"cold_median_ms": tc,
+                               "cold_hbm_frac": byts / (tc / 1e3) / 1e9 / HBM_PEAK_GBS})
     del S
     # sparse anchors kept in pinned host memory, gathered over the host link
     pc, wts = config_c5()
@@ -671,6 +700,11 @@ def main():
         entry, seqs, S_ref, o_ref = cpu_baseline(case, args.cpu_budget)
         line["cpu_baseline"] = entry
         line["parity"] = parity_vs_oracle(S, o, case, seqs, S_ref, o_ref)
+    # cold: the headline launch with the caches flushed before each call
+    tc = time_cold(step)
+    line["cold"] = {"note": "headline launch, median of 20 calls each after a 512 MiB write "
+                            "that evicts the infinity cache and L2s",
+                    "median_ms": tc, "hbm_frac": byts / (tc / 1e3) / 1e9 / HBM_PEAK_GBS}
     if not args.no_group:
         # the same headline launch once more at the end of the run, after
         # seconds of other GPU work, as a check that `value` (timed first,
