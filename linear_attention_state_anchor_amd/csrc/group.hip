@@ -13,7 +13,7 @@
 //   z and a|b; gates_kernel forms the gates)
 //   S, o = gated delta rule from S_0 = 0                   launch_gdn_chunk
 //   y    = rms(o) o SiLU(P_z) per value head               gated_norm_kernel
-//   D    = y W_out (fp32); x <- x + D in the next RMSNorm   gemm_kernel (MFMA)
+//   x    = x + y W_out (fp32, in the projection's epilogue) gemm_kernel (MFMA)
 // The last GDN layer of the group only needs its state: its projection
 // covers the k|v|a|b prefix of the packed columns (plus q when the conv
 // windows are returned) and no output is formed.
@@ -165,45 +165,30 @@ __device__ __forceinline__ void load8f<F32>(const void* x, size_t idx, float (&v
   }
 }
 
-// ADD: the row is x + D (D fp32: the previous layer's output projection),
-// and the sum is also written back to xres (the fp32 residual stream; it
-// may alias x).
-template <typename TX, bool ADD>
-__global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, const float* __restrict__ dlt,
-                                                       int rows, int cols, float eps,
-                                                       float* xres, _Float16* __restrict__ xh) {
+// One row per wave: the RMSNorm of x (the anchors in bf16, or the fp32
+// residual stream) in fp16, the A operand of the next projection.
+template <typename TX>
+__global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, int rows, int cols,
+                                                       float eps, _Float16* __restrict__ xh) {
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (row >= rows) return;
   const size_t base = static_cast<size_t>(row) * cols;
-  auto load = [&](int c, float (&v)[8]) {
-    load8f<TX>(x, base + c, v);
-    if (ADD) {
-      float dv[8];
-      load8f<F32>(dlt, base + c, dv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += dv[e];
-    }
-  };
   float s = 0.0f;
   for (int c = 8 * lane; c < cols; c += 8 * kWave) {
     float v[8];
-    load(c, v);
+    load8f<TX>(x, base + c, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf(v[e], v[e], s);
   }
   const float r = rsqrtf(wave_sum(s) / static_cast<float>(cols) + eps);
   for (int c = 8 * lane; c < cols; c += 8 * kWave) {
     float v[8];
-    load(c, v);
+    load8f<TX>(x, base + c, v);
     f16x8 h;
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(v[e] * r);
     *reinterpret_cast<f16x8*>(xh + base + c) = h;
-    if (ADD) {
-      *reinterpret_cast<f32x4*>(xres + base + c) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(xres + base + c + 4) = f32x4{v[4], v[5], v[6], v[7]};
-    }
   }
 }
 
@@ -212,6 +197,9 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, const floa
 // accumulation.
 //   EPI_STORE16: C fp16 = acc
 //   EPI_STORE32: C fp32 = acc
+//   EPI_ADD_F32, EPI_ADD_BF16: C fp32 = X + acc (the residual add of a
+//                block's output projection; X fp32, in place allowed, or
+//                the bf16 anchors)
 //   EPI_SWIGLU:  B's rows alternate gate and up columns in pairs, so the
 //                4 consecutive results of a lane are (g_c, u_c, g_c+1,
 //                u_c+1); C fp16 [M][N/2] = SiLU(g) * u (the FFN's gated
@@ -235,6 +223,10 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, const floa
 constexpr int EPI_STORE16 = 0;
 constexpr int EPI_STORE32 = 1;
 constexpr int EPI_SWIGLU = 2;
+// residual adds: C = X + A B^T in fp32, X fp32 (may be C itself: each element
+// is read and written by the same thread) or bf16 (the anchors)
+constexpr int EPI_ADD_F32 = 3;
+constexpr int EPI_ADD_BF16 = 4;
 constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8;
 constexpr int GGROUP = 8;  // M-tiles per group of the tile order
 constexpr int kXcdG = 8;   // XCDs
@@ -453,7 +445,8 @@ template <int EPI, int NJ>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict__ A, int lda,
                                                       const _Float16* __restrict__ Bt, int ldb,
                                                       int M, int N, int K, void* C, int ldc,
-                                                      int q_begin, int q_count) {
+                                                      const void* X, int ldx, int q_begin,
+                                                      int q_count) {
   constexpr int BN = 64 * NJ;                 // columns of the workgroup
   __shared__ _Float16 sm[2 * (GBM * GLD + BN * GLD)];  // [buffer][A rows | B rows]
   const int tid = threadIdx.x;
@@ -500,6 +493,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
           const f16x2 h = {static_cast<_Float16>(silu(v[0]) * v[1]),
                            static_cast<_Float16>(silu(v[2]) * v[3])};
           *reinterpret_cast<f16x2*>(static_cast<_Float16*>(C) + static_cast<size_t>(m) * ldc + n / 2) = h;
+        } else if (EPI == EPI_ADD_F32 || EPI == EPI_ADD_BF16) {
+          const size_t xi = static_cast<size_t>(m) * ldx + n;
+          f32x4 x;
+          if (EPI == EPI_ADD_F32) {
+            x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(X) + xi);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = load1<BF16>(X, xi + e);
+          }
+          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + ci) = x + v;
         } else {
           *reinterpret_cast<f32x4*>(static_cast<float*>(C) + ci) = v;
         }
@@ -876,13 +879,6 @@ __global__ void seq_start_kernel(const int32_t* __restrict__ cu, int n_seqs, int
 
 // out = x + dlt (the group's output hidden state: the last layer's residual
 // stream plus its output projection), fp32
-template <typename TX>
-__global__ __launch_bounds__(256) void residual_out_kernel(const void* x, const float* __restrict__ dlt,
-                                                           size_t count, float* __restrict__ out) {
-  for (size_t e = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; e < count;
-       e += static_cast<size_t>(gridDim.x) * blockDim.x)
-    out[e] = load1<TX>(x, e) + dlt[e];
-}
 
 // y = o / sqrt(mean(o^2) + eps) * SiLU(z), per (token, value head), fp16 out;
 // z is read from the projection rows (columns z_off + head * D).  A wave
@@ -923,7 +919,7 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(const _Float16* __restr
 // workspace layout of one group call
 // ---------------------------------------------------------------------------
 struct Workspace {
-  size_t xres, dres, xh, p, q, k, v, la, be, o, y, ss, sid, total;
+  size_t xres, xh, p, q, k, v, la, be, o, y, ss, sid, total;
 };
 
 // (the FFN's gated product [T][F] fp16 reuses the projection rows, dead by
@@ -938,7 +934,6 @@ Workspace plan(const LayerShape& L, int T, int ffn_dim) {
   };
   const size_t t = static_cast<size_t>(T);
   w.xres = take(t * L.hidden * 4);
-  w.dres = take(t * L.hidden * 4);
   w.xh = take(t * L.hidden * 2);
   w.p = take(t * static_cast<size_t>(std::max(L.n_all(), ffn_dim)) * 2);
   w.q = take(t * L.h_k * L.d * 2);
@@ -956,7 +951,7 @@ Workspace plan(const LayerShape& L, int T, int ffn_dim) {
 
 template <int EPI>
 hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, int N, int K,
-                void* C, int ldc, hipStream_t s) {
+                void* C, int ldc, hipStream_t s, const void* X = nullptr, int ldx = 0) {
   if (M == 0 || N == 0) return hipSuccess;
   // the kernel addresses A and Bt with 32-bit byte offsets: split M so that
   // every launch stays below 2^31 bytes of A
@@ -977,21 +972,25 @@ hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, 
       full = tiles - rest;
       narrow = rest;
     }
-    void* Cm = EPI == EPI_STORE32
-                   ? static_cast<void*>(static_cast<float*>(C) + static_cast<size_t>(m_at) * ldc)
+    constexpr bool c32 = EPI == EPI_STORE32 || EPI == EPI_ADD_F32 || EPI == EPI_ADD_BF16;
+    void* Cm = c32 ? static_cast<void*>(static_cast<float*>(C) + static_cast<size_t>(m_at) * ldc)
                    : static_cast<void*>(static_cast<_Float16*>(C) + static_cast<size_t>(m_at) * ldc);
+    const void* Xm =
+        EPI == EPI_ADD_F32    ? static_cast<const void*>(static_cast<const float*>(X) + static_cast<size_t>(m_at) * ldx)
+        : EPI == EPI_ADD_BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(X) + static_cast<size_t>(m_at) * ldx)
+                              : nullptr;
     const _Float16* Am = A + static_cast<size_t>(m_at) * lda;
     if (full > 0) {
       dim3 grid((full + kXcdG - 1) / kXcdG * kXcdG), block(256);
       hipLaunchKernelGGL((gemm_kernel<EPI, 4>), grid, block, 0, s, Am, lda, Bt, ldb, mm, N, K, Cm,
-                         ldc, 0, full);
+                         ldc, Xm, ldx, 0, full);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
     if (narrow > 0) {
       dim3 grid(narrow * kStrips), block(256);
       hipLaunchKernelGGL((gemm_kernel<EPI, 1>), grid, block, 0, s, Am, lda, Bt, ldb, mm, N, K, Cm,
-                         ldc, full, narrow);
+                         ldc, Xm, ldx, full, narrow);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1110,7 +1109,6 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
   }
   char* ws = static_cast<char*>(workspace);
   float* xres = reinterpret_cast<float*>(ws + W.xres);
-  float* dres = reinterpret_cast<float*>(ws + W.dres);
   _Float16* xh = reinterpret_cast<_Float16*>(ws + W.xh);
   _Float16* P = reinterpret_cast<_Float16*>(ws + W.p);
   _Float16* qb = reinterpret_cast<_Float16*>(ws + W.q);
@@ -1130,23 +1128,32 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
                        d->n_seqs, T, sst, sid);
     if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
   }
-  // The residual stream x starts as the anchors (bf16); each residual add
-  // (x + mixer or FFN output, fp32, in dres) happens inside the RMSNorm that
-  // reads it, which writes the sum to xres.
+  // The residual stream x starts as the anchors (bf16); each block's output
+  // projection adds its output to it in its epilogue, writing the fp32 sum
+  // to xres (in place after the first), or to the group's output buffer for
+  // the group's last block.
   bool x_is_anchors = true;
-  auto norm = [&](bool add) -> bool {
+  auto norm = [&]() -> bool {
     const dim3 rgrid((T + 3) / 4);
-    if (!add)
-      hipLaunchKernelGGL((sr::rms_norm_kernel<sr::BF16, false>), rgrid, dim3(256), 0, s, anchors,
-                         nullptr, T, d->hidden, d->rms_eps, nullptr, xh);
-    else if (x_is_anchors)
-      hipLaunchKernelGGL((sr::rms_norm_kernel<sr::BF16, true>), rgrid, dim3(256), 0, s, anchors,
-                         dres, T, d->hidden, d->rms_eps, xres, xh);
+    if (x_is_anchors)
+      hipLaunchKernelGGL((sr::rms_norm_kernel<sr::BF16>), rgrid, dim3(256), 0, s, anchors, T,
+                         d->hidden, d->rms_eps, xh);
     else
-      hipLaunchKernelGGL((sr::rms_norm_kernel<sr::F32, true>), rgrid, dim3(256), 0, s,
-                         static_cast<const void*>(xres), dres, T, d->hidden, d->rms_eps, xres, xh);
-    if (add) x_is_anchors = false;
+      hipLaunchKernelGGL((sr::rms_norm_kernel<sr::F32>), rgrid, dim3(256), 0, s,
+                         static_cast<const void*>(xres), T, d->hidden, d->rms_eps, xh);
     return hipGetLastError() == hipSuccess;
+  };
+  // x <- x + A B^T: into xres, or into the output buffer when `out` is set
+  auto add_block = [&](const _Float16* A, int lda, const _Float16* Bt, int K, float* out) -> bool {
+    float* C = out ? out : xres;
+    const hipError_t e =
+        x_is_anchors
+            ? sr::gemm<sr::EPI_ADD_BF16>(A, lda, Bt, K, T, d->hidden, K, C, d->hidden, s, anchors,
+                                         d->hidden)
+            : sr::gemm<sr::EPI_ADD_F32>(A, lda, Bt, K, T, d->hidden, K, C, d->hidden, s, xres,
+                                        d->hidden);
+    x_is_anchors = false;
+    return e == hipSuccess;
   };
   for (int li = 0; li < n_gdn; ++li) {
     const bool is_last = li == n_gdn - 1;
@@ -1161,9 +1168,8 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
     float* st = states + state_stride * li;
     if (T > 0) {
       // x of this layer: the anchors for the first, after that the residual
-      // stream plus the previous block's output (dres); xh = RMSNorm(x) in
-      // fp16, the A operand of the projection
-      if (!norm(li > 0)) return SR_ELAUNCH;
+      // stream; xh = RMSNorm(x) in fp16, the A operand of the projection
+      if (!norm()) return SR_ELAUNCH;
       // the last layer needs k|v|a|b for its state, and q as well when its
       // conv window is returned (q follows the state prefix in the packing)
       const int N = full ? L.n_all()
@@ -1265,34 +1271,23 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
                          L.z_off(), d->h_v, rows, d->rms_eps, yb);
     if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
     const int K2 = d->h_v * d->d;
-    // the residual add happens in the next layer's RMSNorm
-    hipError_t e = sr::gemm<sr::EPI_STORE32>(yb, K2, wout, K2, T, d->hidden, K2, dres, d->hidden, s);
-    if (e != hipSuccess) return SR_ELAUNCH;
     // FFN block after the mixer (not after the last layer of a replay: its
     // output is never used there): x <- x + W_down (SiLU(xh W_g) * (xh W_u))
-    if (d->ffn_dim > 0 && weights[li].ffn) {
+    const bool has_ffn = d->ffn_dim > 0 && weights[li].ffn;
+    // x <- x + y W_out; the group's last block writes the sum, the group's
+    // output, to hidden_out
+    if (!add_block(yb, K2, wout, K2, is_last && !has_ffn ? hidden_out : nullptr))
+      return SR_ELAUNCH;
+    if (has_ffn) {
       const int F = d->ffn_dim;
       const _Float16* wgu = static_cast<const _Float16*>(weights[li].ffn);
       const _Float16* wdn = wgu + static_cast<size_t>(2 * F) * d->hidden;
       _Float16* hb = P;  // [T][F] fp16, the projection rows are dead here
-      if (!norm(true)) return SR_ELAUNCH;
+      if (!norm()) return SR_ELAUNCH;
       if (sr::gemm<sr::EPI_SWIGLU>(xh, d->hidden, wgu, d->hidden, T, 2 * F, d->hidden, hb, F, s) !=
           hipSuccess)
         return SR_ELAUNCH;
-      if (sr::gemm<sr::EPI_STORE32>(hb, F, wdn, F, T, d->hidden, F, dres, d->hidden, s) != hipSuccess)
-        return SR_ELAUNCH;
-    }
-    if (is_last) {
-      // the group's output: the residual stream plus the last block's output
-      const size_t count = static_cast<size_t>(T) * d->hidden;
-      const int blocks = static_cast<int>(std::min<size_t>(4096, (count + 255) / 256));
-      if (x_is_anchors)
-        hipLaunchKernelGGL(sr::residual_out_kernel<sr::BF16>, dim3(blocks), dim3(256), 0, s, anchors,
-                           dres, count, hidden_out);
-      else
-        hipLaunchKernelGGL(sr::residual_out_kernel<sr::F32>, dim3(blocks), dim3(256), 0, s,
-                           static_cast<const void*>(xres), dres, count, hidden_out);
-      if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+      if (!add_block(hb, F, wdn, F, is_last ? hidden_out : nullptr)) return SR_ELAUNCH;
     }
   }
   return SR_OK;
