@@ -60,7 +60,8 @@ constexpr int kC = 64;         // chunk length (tokens)
 //  * HP = 1, NW = 8 for at most one chain per CU: 16 value columns per
 //    wave, two waves per SIMD instead of one;
 //  * HP = 1, NW = 4, VS = 2 for at most half a chain per CU: two workgroups
-//    per chain, 16 value columns per wave;
+//    per chain, 16 value columns per wave, plus 4 producer waves per
+//    workgroup (PC) that stage the next chunk and form its tiles;
 //  * HP = 1, NW = 4 otherwise: two workgroups of 4 waves per CU.
 constexpr int kAS = kC + 8;    // fp16 row stride of -A
 constexpr int kPS = kC + 8;    // fp16 row stride of P o QK^T
@@ -429,10 +430,14 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
   }
 }
 
-template <int D, typename TI, typename TO, bool ERASE, bool WANT_O, int HP, int NW, int VS>
-__global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_kernel(
-    GdnArgs a, int units_per_xcd) {
-  constexpr int kThreads = 64 * NW * HP;
+// PC: producer/consumer form (one head, 4 consumer waves, VS = 2): 4 more
+// waves per workgroup stage chunk c + 1 and form its tiles while the 4
+// consumer waves run chunk c's state work, on two LDS buffers.
+template <int D, typename TI, typename TO, bool ERASE, bool WANT_O, int HP, int NW, int VS, bool PC>
+__global__ __launch_bounds__(64 * NW * HP * (PC ? 2 : 1), NW * HP == 4 && !PC ? 2 : 1) void
+gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
+  static_assert(!PC || (HP == 1 && NW == 4), "the producer/consumer form has one head of 4 waves");
+  constexpr int kThreads = 64 * NW * HP;  // (consumer) waves' threads; as many producers in PC
   constexpr int DV = D / VS;      // value columns of the workgroup (per head)
   constexpr int IW = DV / NW;     // value columns per wave
   constexpr int NIT = IW / 16;    // 16-wide column tiles per wave
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
   static_assert(kC * CPR % kThreads == 0 && kThreads % VCP == 0,
                 "staging pieces must divide evenly");
 
-  __shared__ ChunkSmem<D, HP> sm;
+  __shared__ ChunkSmem<D, HP> smb[PC ? 2 : 1];
 
   // XCD-aware numbering: consecutive (sequence, head group) units share an
   // XCD (with one head per workgroup, the value heads of a key head then
@@ -464,7 +469,7 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
   const int g = hb / (a.h_v / a.h_k);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
-  const int hp = w / NW;  // this wave's head within the workgroup
+  const int hp = PC ? 0 : w / NW;  // this wave's head within the workgroup
   const int wq = w % NW;  // this wave within its head
   const int h = hb + hp;
   constexpr bool want_o = WANT_O;
@@ -499,11 +504,12 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
 
   // P o QK^T tiles (0,1) and (2,3) are read as zeros by the K = 32 steps of
   // the output product and never written otherwise
-  for (int e = tid; e < 256 * HP; e += kThreads) {
-    const int hh = e / 256, rr = (e % 256) / 16, cc = e % 16;
-    sm.pqk[hh][rr * kPS + kperm(16 + cc)] = static_cast<_Float16>(0.0f);
-    sm.pqk[hh][(32 + rr) * kPS + kperm(48 + cc)] = static_cast<_Float16>(0.0f);
-  }
+  for (int b = 0; b < (PC ? 2 : 1); ++b)
+    for (int e = tid; e < 256 * HP; e += kThreads) {
+      const int hh = e / 256, rr = (e % 256) / 16, cc = e % 16;
+      smb[b].pqk[hh][rr * kPS + kperm(16 + cc)] = static_cast<_Float16>(0.0f);
+      smb[b].pqk[hh][(32 + rr) * kPS + kperm(48 + cc)] = static_cast<_Float16>(0.0f);
+    }
 
   const int t_begin = a.cu[n];
   const int t_end = a.cu[n + 1];
@@ -514,14 +520,16 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
   u16x8 pk[NPF], pq[NPF], pv[NPFV];
   float pa = 0.0f, pb = 0.0f;
   // this thread's 16-byte piece: row (w*64 + l) / CPR, column 8 * ((w*64 + l) % CPR)
-  auto lane_row = [&]() { return (static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) / CPR; };
-  auto lane_col = [&]() { return 8u * ((static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) % CPR); };
+  // (PC: the producer waves load, numbered from 0)
+  const int lw = PC ? w - NW * HP : w;
+  auto lane_row = [&]() { return (static_cast<unsigned>(lw) * kWave + static_cast<unsigned>(l)) / CPR; };
+  auto lane_col = [&]() { return 8u * ((static_cast<unsigned>(lw) * kWave + static_cast<unsigned>(l)) % CPR); };
   // byte offsets from a uniform row base: 32-bit and unsigned, so the loads
   // take the scalar-base + vector-offset form without 64-bit address math
   auto kq_off = [&]() { return 2u * (lane_row() * static_cast<unsigned>(qk_row) + lane_col()); };
   // V: this thread's piece of a token row of all the workgroup's heads
-  auto v_lane_row = [&]() { return (static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) / VCP; };
-  auto v_lane_piece = [&]() { return (static_cast<unsigned>(w) * kWave + static_cast<unsigned>(l)) % VCP; };
+  auto v_lane_row = [&]() { return (static_cast<unsigned>(lw) * kWave + static_cast<unsigned>(l)) / VCP; };
+  auto v_lane_piece = [&]() { return (static_cast<unsigned>(lw) * kWave + static_cast<unsigned>(l)) % VCP; };
   auto v_off = [&]() {
     const unsigned cp = v_lane_piece();
     return 2u * (v_lane_row() * static_cast<unsigned>(v_row) + static_cast<unsigned>(D) * (cp / VCPH) +
@@ -605,315 +613,367 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
       n_dec = __expf(gC - gl);
     }
   };
-  if (t_begin < t_end) {
+  if (t_begin < t_end && (!PC || w >= NW * HP)) {
     prefetch_all(t_begin);
     prepare(t_begin);
   }
   int sexp = 0;  // state exponent E of this wave (S = 2^E S_reg)
 
-  for (int c0 = t_begin; c0 < t_end; c0 += kC) {
-    const int nv = min(kC, t_end - c0);
-    // Re-derive the lane coordinates each chunk through an opaque copy so
-    // that the many lane-dependent LDS/global addresses are recomputed in the
-    // loop instead of being hoisted out of it (which would pin one register
-    // per address for the whole sequence).
-    int tro, trv;  // this lane's transpose-read offsets in the K and V tiles
-    {
-      unsigned t_ = tid;
-      asm volatile("" : "+v"(t_));
-      l = t_ & (kWave - 1);
-      lr = t_ & 15;
-      lg = (t_ >> 4) & 3;
-      // K transpose reads: token row (l >> 2) of a 16-row block, the 4 keys
-      // kkey(jt, l & 3, 0..3) (8 (l & 3) + a per-tile constant), swizzled
-      tro = (l >> 2) * ChunkSmem<D, HP>::kKS + ((8 * (l & 3)) ^ kswz(l >> 2));
-      trv = (l >> 2) * kWS + 4 * (l & 3);
-    }
-
-    // ---- stage this chunk: K, Q, V rows (already fp16) and gate scalars --
+  // ---- the pieces of one chunk ------------------------------------------
+  // The plain launch runs them in order for each chunk with barriers in
+  // between; the producer/consumer launch (PC) runs the staging and tiles of
+  // chunk c + 1 (producer waves) beside the state work of chunk c (consumer
+  // waves), on two LDS buffers.
+  int tro = 0, trv = 0;  // this lane's transpose-read offsets in the K and V tiles
+  // U accumulators: tile (tt, it) = token rows 16tt.., value columns
+  // w*IW + 16it..
+  f32x4 U[4][NIT];
+  // fp16 copy of the state (B operand of K S^T, A operand of the outputs),
+  // converted once per chunk
+  f16x8 S16[NKJ][NIT];
+  float s_dn = 1.0f, s_up = 1.0f;
+  // the next chunk's loads are issued in slots spread over the compute: pfn
+  // is the next slot, pf_c0 the chunk they load (none when !pf_more)
+  int pfn = 0, pf_c0 = 0;
+  bool pf_more = false;
+  auto pf_next = [&](int n) {
 #pragma unroll
-    for (int e = 0; e < NPF; ++e) {
-      const unsigned row = lane_row() + (kThreads / CPR) * e, col = lane_col();
-      lds_store16(lds_addr(sm.k) + 2 * (row * ChunkSmem<D, HP>::kKS + (col ^ kswz(row))), pk[e]);
-      if (want_o) lds_store16(lds_addr(sm.q) + 2 * (row * ChunkSmem<D, HP>::kQS + col), pq[e]);
+    for (int i = 0; i < n; ++i) {
+      if (pf_more && pfn < kSlots) pf_slot(pfn, pf_c0);
+      ++pfn;
     }
-#pragma unroll
-    for (int e = 0; e < NPFV; ++e) {
-      const unsigned row = v_lane_row() + (kThreads / VCP) * e, cp = v_lane_piece();
-      lds_store16(lds_addr(&sm.w[cp / VCPH][0]) + 2 * (row * kWS + col0 + 8 * (cp % VCPH)), pv[e]);
-    }
-    if (wq == 0) {
-      sm.gcum[hp][l] = n_g;
-      sm.gam[hp][l] = n_eg;
-      sm.dec[hp][l] = n_dec;
-      sm.beta[hp][l] = n_be;
-    }
-    __syncthreads();
-
-    // the next chunk's gates, K, Q and V fly while this one computes; slot
-    // pfn is the next load to issue
-    const bool more = c0 + kC < t_end;
-    int pfn = 0;
-    auto pf_next = [&](int n) {
-#pragma unroll
-      for (int i = 0; i < n; ++i) {
-        if (more && pfn < kSlots) pf_slot(pfn, c0 + kC);
-        ++pfn;
+  };
+  auto coords = [&]() {
+      // Re-derive the lane coordinates each chunk through an opaque copy so
+      // that the many lane-dependent LDS/global addresses are recomputed in the
+      // loop instead of being hoisted out of it (which would pin one register
+      // per address for the whole sequence).
+      {
+        unsigned t_ = tid;
+        asm volatile("" : "+v"(t_));
+        l = t_ & (kWave - 1);
+        lr = t_ & 15;
+        lg = (t_ >> 4) & 3;
+        // K transpose reads: token row (l >> 2) of a 16-row block, the 4 keys
+        // kkey(jt, l & 3, 0..3) (8 (l & 3) + a per-tile constant), swizzled
+        tro = (l >> 2) * ChunkSmem<D, HP>::kKS + ((8 * (l & 3)) ^ kswz(l >> 2));
+        trv = (l >> 2) * kWS + 4 * (l & 3);
       }
-    };
-    if (more) pf_gates(c0 + kC);
-    pf_next(2);
-
-    // ---- A (erase) and P o QK^T: lower-triangular 16x16 tiles -------------
-    // Every wave forms the diagonal block of its head's rows 16 (w % 4)..
-    // and inverts it (a wave-local LDS round trip, no barrier), and takes its
-    // share of the off-diagonal A tiles and the P o QK^T tiles.
-    switch (w) {
-      case 0: chunk_tiles<D, HP, NW, ERASE, WANT_O, 0>(sm, lr, lg, a.scale); break;
-      case 1: chunk_tiles<D, HP, NW, ERASE, WANT_O, 1>(sm, lr, lg, a.scale); break;
-      case 2: chunk_tiles<D, HP, NW, ERASE, WANT_O, 2>(sm, lr, lg, a.scale); break;
-      case 3: chunk_tiles<D, HP, NW, ERASE, WANT_O, 3>(sm, lr, lg, a.scale); break;
-      case 4: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 4>(sm, lr, lg, a.scale); break;
-      case 5: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 5>(sm, lr, lg, a.scale); break;
-      case 6: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 6>(sm, lr, lg, a.scale); break;
-      default: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 7>(sm, lr, lg, a.scale); break;
-    }
-    __syncthreads();
-
-    // ---- state exponent check (S = 2^E S_reg) -----------------------------
-    {
-      float m = 0.0f;
+  };
+  auto stage = [&](ChunkSmem<D, HP>& sm) {
+      // ---- stage this chunk: K, Q, V rows (already fp16) and gate scalars --
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
+      for (int e = 0; e < NPF; ++e) {
+        const unsigned row = lane_row() + (kThreads / CPR) * e, col = lane_col();
+        lds_store16(lds_addr(sm.k) + 2 * (row * ChunkSmem<D, HP>::kKS + (col ^ kswz(row))), pk[e]);
+        if (want_o) lds_store16(lds_addr(sm.q) + 2 * (row * ChunkSmem<D, HP>::kQS + col), pq[e]);
+      }
 #pragma unroll
-        for (int it = 0; it < NIT; ++it)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(S[jt][it][r]));
-      const bool over = __builtin_amdgcn_ballot_w64(m > kSHi) != 0;
-      const bool under = sexp > 0 && __builtin_amdgcn_ballot_w64(m >= kSLo) == 0;
-      if (over || under) {
-        // rare: rescale S_reg so that its maximum lands just under 2^kSTarget
-        const float mw = wave_max_nonneg(m);
-        int e = 0;
-        (void)frexpf(mw, &e);  // mw < 2^e
-        int k = (mw > 0.0f && mw <= 3.0e38f) ? e - kSTarget : -sexp;
-        k = max(k, -sexp);     // E stays >= 0
-        k = min(k, 100);
-        k = __builtin_amdgcn_readfirstlane(k);
-        sexp += k;
-        const float f = ldexpf(1.0f, -k);
+      for (int e = 0; e < NPFV; ++e) {
+        const unsigned row = v_lane_row() + (kThreads / VCP) * e, cp = v_lane_piece();
+        lds_store16(lds_addr(&sm.w[cp / VCPH][0]) + 2 * (row * kWS + col0 + 8 * (cp % VCPH)), pv[e]);
+      }
+      if (wq == 0) {
+        sm.gcum[hp][l] = n_g;
+        sm.gam[hp][l] = n_eg;
+        sm.dec[hp][l] = n_dec;
+        sm.beta[hp][l] = n_be;
+      }
+  };
+  auto tiles = [&](ChunkSmem<D, HP>& sm) {
+      // ---- A (erase) and P o QK^T: lower-triangular 16x16 tiles -------------
+      // Every wave forms the diagonal block of its head's rows 16 (w % 4)..
+      // and inverts it (a wave-local LDS round trip, no barrier), and takes its
+      // share of the off-diagonal A tiles and the P o QK^T tiles.
+      switch (PC ? w - NW * HP : w) {
+        case 0: chunk_tiles<D, HP, NW, ERASE, WANT_O, 0>(sm, lr, lg, a.scale); break;
+        case 1: chunk_tiles<D, HP, NW, ERASE, WANT_O, 1>(sm, lr, lg, a.scale); break;
+        case 2: chunk_tiles<D, HP, NW, ERASE, WANT_O, 2>(sm, lr, lg, a.scale); break;
+        case 3: chunk_tiles<D, HP, NW, ERASE, WANT_O, 3>(sm, lr, lg, a.scale); break;
+        case 4: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 4>(sm, lr, lg, a.scale); break;
+        case 5: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 5>(sm, lr, lg, a.scale); break;
+        case 6: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 6>(sm, lr, lg, a.scale); break;
+        default: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 7>(sm, lr, lg, a.scale); break;
+      }
+  };
+  auto part1 = [&](ChunkSmem<D, HP>& sm) {
+      // ---- state exponent check (S = 2^E S_reg) -----------------------------
+      {
+        float m = 0.0f;
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-          for (int it = 0; it < NIT; ++it) S[jt][it] *= f;
+          for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(S[jt][it][r]));
+        const bool over = __builtin_amdgcn_ballot_w64(m > kSHi) != 0;
+        const bool under = sexp > 0 && __builtin_amdgcn_ballot_w64(m >= kSLo) == 0;
+        if (over || under) {
+          // rare: rescale S_reg so that its maximum lands just under 2^kSTarget
+          const float mw = wave_max_nonneg(m);
+          int e = 0;
+          (void)frexpf(mw, &e);  // mw < 2^e
+          int k = (mw > 0.0f && mw <= 3.0e38f) ? e - kSTarget : -sexp;
+          k = max(k, -sexp);     // E stays >= 0
+          k = min(k, 100);
+          k = __builtin_amdgcn_readfirstlane(k);
+          sexp += k;
+          const float f = ldexpf(1.0f, -k);
+#pragma unroll
+          for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) S[jt][it] *= f;
+        }
       }
-    }
-    // 2^-E: applied to V (so U is in the state's units); 2^E: to the outputs
-    const float s_dn = ldexpf(1.0f, -sexp);
-    const float s_up = ldexpf(1.0f, sexp);
+      // 2^-E: applied to V (so U is in the state's units); 2^E: to the outputs
+      s_dn = ldexpf(1.0f, -sexp);
+      s_up = ldexpf(1.0f, sexp);
 
-    // U accumulators: tile (tt, it) = token rows 16tt.., value columns
-    // w*IW + 16it..
-    f32x4 U[4][NIT];
-    // fp16 copy of the state (B operand of K S^T, A operand of the outputs),
-    // converted once per chunk
-    f16x8 S16[NKJ][NIT];
 #pragma unroll
-    for (int kk = 0; kk < NKJ; ++kk)
+      for (int kk = 0; kk < NKJ; ++kk)
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) S16[kk][it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
-    // transpose-read base of this lane in the V tile at this wave's columns
-    const uint32_t xv = tr_base(lds_addr(&sm.w[hp][0]) + 2 * (col0 + wq * IW + trv));
-    if (ERASE) {
-      // ---- right-hand side R~ = V - diag(e^G) K S^T ------------------------
-      // K S^T for this wave's value columns, one key k-step at a time: S^T
-      // tiles 2kk and 2kk+1 form the fp16 B operand of k-step kk, K rows the
-      // A operand in the same k order.
+        for (int it = 0; it < NIT; ++it) S16[kk][it] = to_f16x8(S[2 * kk][it], S[2 * kk + 1][it]);
+      // transpose-read base of this lane in the V tile at this wave's columns
+      const uint32_t xv = tr_base(lds_addr(&sm.w[hp][0]) + 2 * (col0 + wq * IW + trv));
+      if (ERASE) {
+        // ---- right-hand side R~ = V - diag(e^G) K S^T ------------------------
+        // K S^T for this wave's value columns, one key k-step at a time: S^T
+        // tiles 2kk and 2kk+1 form the fp16 B operand of k-step kk, K rows the
+        // A operand in the same k order.
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) U[tt][it] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NKJ; ++kk) {
-        SR_SCHED_FENCE();
-        pf_next(1);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int t = 16 * tt + lr;
-          const f16x8 kb = lds8(&sm.k[kidx<D>(t, (32 * kk + 8 * lg) ^ kswz(t))]);
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(kb, S16[kk][it], U[tt][it]);
-        }
-      }
-    }
-    // erase: R~ = 2^-E V - e^G (K S_reg^T) (b is applied by the solve);
-    // erase-free: U = 2^-E diag(b) V.  The 2^-E factor is exact; the
-    // unscaled variant is the common one (E = 0).
-    auto rhs_v = [&](auto scaled) {
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[hp][16 * tt + 4 * lg]);
-        const f32x4 ga4 = *reinterpret_cast<const f32x4*>(&sm.gam[hp][16 * tt + 4 * lg]);
-        if constexpr (decltype(scaled)::value && !ERASE) be4 *= s_dn;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const u16x4 vx = lds_tr4(xv, 2 * (16 * tt * kWS + 16 * it));
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float vv = raw_to_f32<TI>(vx[r]);
-            if constexpr (decltype(scaled)::value && ERASE) vv *= s_dn;
-            U[tt][it][r] = ERASE ? fmaf(-ga4[r], U[tt][it][r], vv) : vv * be4[r];
-          }
-          // pinned in fp32: the solve rounds it to fp16, and a fused
-          // FMA-with-conversion in some template instances only would make
-          // the state-only and full replays differ in the last bit
-          asm volatile("" : "+v"(U[tt][it]));
-        }
-      }
-    };
-    if (sexp == 0) rhs_v(std::false_type{});
-    else rhs_v(std::true_type{});
-    tr_keep(xv);
-    if (ERASE) {
-      // ---- block forward substitution (I + A) U = diag(b) R~, this wave's
-      // columns.  Block row i: U_i = [(I + A_ii)^{-1} diag(b_i)] (R~_i +
-      // sum_{m<i} (-A~_im) U_m); the solved rows return as fp16 B operands.
-      f16x4 Yh[3][NIT];
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        pf_next(1);
-        f32x4 X[NIT];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) X[it] = U[bi][it];
-        const _Float16* arow = &sm.a[hp][(16 * bi + lr) * kAS];
-        if (bi == 1) {
-          const f16x4 a4 = lds4(arow + 8 * lg);
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x16(a4, Yh[0][it], X[it]);
-        } else if (bi >= 2) {
-          const f16x8 a8 = lds8(arow + 8 * lg);
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x32(a8, cat44(Yh[0][it], Yh[1][it]), X[it]);
-          if (bi == 3) {
-            // the third term as a K = 32 product with zero upper k-slots:
-            // accumulating a 16x16x16 MFMA onto a 16x16x32 result (or the
-            // reverse) reads two stale accumulator registers on gfx950 unless
-            // about five wait states separate them, which the compiler does
-            // not insert; same-shape accumulation chains are safe
-            const f16x4 z4 = {};
-            const f16x8 a8z = cat44(lds4(arow + 32 + 8 * lg), z4);
-#pragma unroll
-            for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x32(a8z, cat44(Yh[2][it], z4), X[it]);
-          }
-        }
-        const f16x4 t4 = lds4(&sm.td[hp][bi * 256 + lr * 16 + 4 * lg]);
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          U[bi][it] = mfma16x16x16(t4, to_f16x4(X[it]), f32x4{0.f, 0.f, 0.f, 0.f});
-          if (bi < 3) Yh[bi][it] = to_f16x4(U[bi][it]);
-        }
-      }
-    }
-    pf_next(kSlots);  // whatever is left
-    // U as fp16 B operands: plain (output) and scaled by e^{G_C-G} (state)
-    f16x8 U16[2][NIT], UD[2][NIT];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        f32x4 lo = U[2 * ks][it], hi = U[2 * ks + 1][it];
-        if (want_o) U16[ks][it] = to_f16x8(lo, hi);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          lo[r] *= sm.dec[hp][32 * ks + 4 * lg + r];
-          hi[r] *= sm.dec[hp][32 * ks + 16 + 4 * lg + r];
-        }
-        UD[ks][it] = to_f16x8(lo, hi);
-        // materialise the fp16 copies here so the fp32 U dies now instead of
-        // staying live through the output product
-        asm volatile("" : "+v"(UD[ks][it]));
-        if (want_o) asm volatile("" : "+v"(U16[ks][it]));
-      }
-
-    // ---- O^T = S Q^T diag(e^G) + U^T (P o Q K^T)^T, two token tiles at a
-    // time.  Computing the transpose puts 4 consecutive value columns of one
-    // token in each lane, so every lane stores 8 contiguous bytes.
-    if (want_o) {
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        f32x4 O[2][NIT];  // tile (u, it): value rows w*IW+16it+4lg+r, token column
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) O[u][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int it = 0; it < NIT; ++it) U[tt][it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKJ; ++kk) {
+          SR_SCHED_FENCE();
+          pf_next(1);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const int t = 16 * tt + lr;
+            const f16x8 kb = lds8(&sm.k[kidx<D>(t, (32 * kk + 8 * lg) ^ kswz(t))]);
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) U[tt][it] = mfma16x16x32(kb, S16[kk][it], U[tt][it]);
+          }
+        }
+      }
+      // erase: R~ = 2^-E V - e^G (K S_reg^T) (b is applied by the solve);
+      // erase-free: U = 2^-E diag(b) V.  The 2^-E factor is exact; the
+      // unscaled variant is the common one (E = 0).
+      auto rhs_v = [&](auto scaled) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          f32x4 be4 = *reinterpret_cast<const f32x4*>(&sm.beta[hp][16 * tt + 4 * lg]);
+          const f32x4 ga4 = *reinterpret_cast<const f32x4*>(&sm.gam[hp][16 * tt + 4 * lg]);
+          if constexpr (decltype(scaled)::value && !ERASE) be4 *= s_dn;
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            const u16x4 vx = lds_tr4(xv, 2 * (16 * tt * kWS + 16 * it));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float vv = raw_to_f32<TI>(vx[r]);
+              if constexpr (decltype(scaled)::value && ERASE) vv *= s_dn;
+              U[tt][it][r] = ERASE ? fmaf(-ga4[r], U[tt][it][r], vv) : vv * be4[r];
+            }
+            // pinned in fp32: the solve rounds it to fp16, and a fused
+            // FMA-with-conversion in some template instances only would make
+            // the state-only and full replays differ in the last bit
+            asm volatile("" : "+v"(U[tt][it]));
+          }
+        }
+      };
+      if (sexp == 0) rhs_v(std::false_type{});
+      else rhs_v(std::true_type{});
+      tr_keep(xv);
+      if (ERASE) {
+        // ---- block forward substitution (I + A) U = diag(b) R~, this wave's
+        // columns.  Block row i: U_i = [(I + A_ii)^{-1} diag(b_i)] (R~_i +
+        // sum_{m<i} (-A~_im) U_m); the solved rows return as fp16 B operands.
+        f16x4 Yh[3][NIT];
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi) {
+          pf_next(1);
+          f32x4 X[NIT];
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) X[it] = U[bi][it];
+          const _Float16* arow = &sm.a[hp][(16 * bi + lr) * kAS];
+          if (bi == 1) {
+            const f16x4 a4 = lds4(arow + 8 * lg);
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x16(a4, Yh[0][it], X[it]);
+          } else if (bi >= 2) {
+            const f16x8 a8 = lds8(arow + 8 * lg);
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x32(a8, cat44(Yh[0][it], Yh[1][it]), X[it]);
+            if (bi == 3) {
+              // the third term as a K = 32 product with zero upper k-slots:
+              // accumulating a 16x16x16 MFMA onto a 16x16x32 result (or the
+              // reverse) reads two stale accumulator registers on gfx950 unless
+              // about five wait states separate them, which the compiler does
+              // not insert; same-shape accumulation chains are safe
+              const f16x4 z4 = {};
+              const f16x8 a8z = cat44(lds4(arow + 32 + 8 * lg), z4);
+#pragma unroll
+              for (int it = 0; it < NIT; ++it) X[it] = mfma16x16x32(a8z, cat44(Yh[2][it], z4), X[it]);
+            }
+          }
+          const f16x4 t4 = lds4(&sm.td[hp][bi * 256 + lr * 16 + 4 * lg]);
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            U[bi][it] = mfma16x16x16(t4, to_f16x4(X[it]), f32x4{0.f, 0.f, 0.f, 0.f});
+            if (bi < 3) Yh[bi][it] = to_f16x4(U[bi][it]);
+          }
+        }
+      }
+      pf_next(kSlots);  // whatever is left
+  };
+  auto part2 = [&](ChunkSmem<D, HP>& sm, int c0) {
+    const int nv = min(kC, t_end - c0);
+      // U as fp16 B operands: plain (output) and scaled by e^{G_C-G} (state)
+      f16x8 U16[2][NIT], UD[2][NIT];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          f32x4 lo = U[2 * ks][it], hi = U[2 * ks + 1][it];
+          if (want_o) U16[ks][it] = to_f16x8(lo, hi);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            lo[r] *= sm.dec[hp][32 * ks + 4 * lg + r];
+            hi[r] *= sm.dec[hp][32 * ks + 16 + 4 * lg + r];
+          }
+          UD[ks][it] = to_f16x8(lo, hi);
+          // materialise the fp16 copies here so the fp32 U dies now instead of
+          // staying live through the output product
+          asm volatile("" : "+v"(UD[ks][it]));
+          if (want_o) asm volatile("" : "+v"(U16[ks][it]));
+        }
+
+      // ---- O^T = S Q^T diag(e^G) + U^T (P o Q K^T)^T, two token tiles at a
+      // time.  Computing the transpose puts 4 consecutive value columns of one
+      // token in each lane, so every lane stores 8 contiguous bytes.
+      if (want_o) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          f32x4 O[2][NIT];  // tile (u, it): value rows w*IW+16it+4lg+r, token column
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) O[u][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NKJ; ++kk) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int t = 16 * (2 * tp + u) + lr;
+              const f16x8 qb = lds8(&sm.q[qidx<D>(t, 32 * kk + 8 * lg)]);
+#pragma unroll
+              for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(S16[kk][it], qb, O[u][it]);
+            }
+          }
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const int t = 16 * (2 * tp + u) + lr;
-            const f16x8 qb = lds8(&sm.q[qidx<D>(t, 32 * kk + 8 * lg)]);
+            const int tt = 2 * tp + u;
+            const int t = 16 * tt + lr;
+            const float gt = a.scale * sm.gam[hp][t];
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(S16[kk][it], qb, O[u][it]);
+            for (int it = 0; it < NIT; ++it) O[u][it] *= gt;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              if (32 * ks > 16 * tt + 15) continue;  // P o QK^T is lower triangular
+              const _Float16* pr = &sm.pqk[hp][t * kPS + 32 * ks];
+              const f16x8 pb = lds8(pr + 8 * lg);
+#pragma unroll
+              for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(U16[ks][it], pb, O[u][it]);
+            }
+            if (sexp != 0) {  // back from the state's units (exact)
+#pragma unroll
+              for (int it = 0; it < NIT; ++it) O[u][it] *= s_up;
+            }
+            if (t < nv) {
+              // uniform base (this chunk, this head) + 32-bit lane offset
+              constexpr unsigned kOB = std::is_same<TO, F32>::value ? 4u : 2u;
+              char* ob0 = static_cast<char*>(a.o) + (static_cast<size_t>(c0) * a.h_v + h) * D * kOB;
+              const unsigned oo = kOB * (static_cast<unsigned>(t) * static_cast<unsigned>(a.h_v) * D +
+                                         static_cast<unsigned>(col0 + wq * IW + 4 * lg));
+#pragma unroll
+              for (int it = 0; it < NIT; ++it) store4<TO>(ob0 + oo + kOB * 16 * it, 0, O[u][it]);
+            }
           }
         }
+      }
+
+      // ---- S^T <- e^{G_C} S^T + K^T diag(e^{G_C-G}) U -----------------------
+      {
+        const float gC = sm.gam[hp][kC - 1];
+        const uint32_t sb = tr_base(lds_addr(sm.k) + 2 * tro);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int tt = 2 * tp + u;
-          const int t = 16 * tt + lr;
-          const float gt = a.scale * sm.gam[hp][t];
+        for (int jt = 0; jt < NJT; ++jt) {
+          SR_SCHED_FENCE();
 #pragma unroll
-          for (int it = 0; it < NIT; ++it) O[u][it] *= gt;
+          for (int it = 0; it < NIT; ++it) S[jt][it] *= gC;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            if (32 * ks > 16 * tt + 15) continue;  // P o QK^T is lower triangular
-            const _Float16* pr = &sm.pqk[hp][t * kPS + 32 * ks];
-            const f16x8 pb = lds8(pr + 8 * lg);
+            // K^T rows kkey(jt, ..), token k-slots {32ks+4lg.., 32ks+16+4lg..}
+            constexpr int KS = ChunkSmem<D, HP>::kKS;
+            const int kc = kkey(jt, 0, 0);
+            const f16x8 av = cat44(as_f16x4(lds_tr4(sb, 2 * (32 * ks * KS + kc))),
+                                   as_f16x4(lds_tr4(sb, 2 * ((32 * ks + 16) * KS + kc))));
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) O[u][it] = mfma16x16x32(U16[ks][it], pb, O[u][it]);
-          }
-          if (sexp != 0) {  // back from the state's units (exact)
-#pragma unroll
-            for (int it = 0; it < NIT; ++it) O[u][it] *= s_up;
-          }
-          if (t < nv) {
-            // uniform base (this chunk, this head) + 32-bit lane offset
-            constexpr unsigned kOB = std::is_same<TO, F32>::value ? 4u : 2u;
-            char* ob0 = static_cast<char*>(a.o) + (static_cast<size_t>(c0) * a.h_v + h) * D * kOB;
-            const unsigned oo = kOB * (static_cast<unsigned>(t) * static_cast<unsigned>(a.h_v) * D +
-                                       static_cast<unsigned>(col0 + wq * IW + 4 * lg));
-#pragma unroll
-            for (int it = 0; it < NIT; ++it) store4<TO>(ob0 + oo + kOB * 16 * it, 0, O[u][it]);
+            for (int it = 0; it < NIT; ++it) S[jt][it] = mfma16x16x32(av, UD[ks][it], S[jt][it]);
           }
         }
+        tr_keep(sb);
       }
-    }
+  };
 
-    // ---- S^T <- e^{G_C} S^T + K^T diag(e^{G_C-G}) U -----------------------
-    {
-      const float gC = sm.gam[hp][kC - 1];
-      const uint32_t sb = tr_base(lds_addr(sm.k) + 2 * tro);
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        SR_SCHED_FENCE();
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) S[jt][it] *= gC;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          // K^T rows kkey(jt, ..), token k-slots {32ks+4lg.., 32ks+16+4lg..}
-          constexpr int KS = ChunkSmem<D, HP>::kKS;
-          const int kc = kkey(jt, 0, 0);
-          const f16x8 av = cat44(as_f16x4(lds_tr4(sb, 2 * (32 * ks * KS + kc))),
-                                 as_f16x4(lds_tr4(sb, 2 * ((32 * ks + 16) * KS + kc))));
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) S[jt][it] = mfma16x16x32(av, UD[ks][it], S[jt][it]);
-        }
-      }
-      tr_keep(sb);
+  if constexpr (!PC) {
+    for (int c0 = t_begin; c0 < t_end; c0 += kC) {
+      coords();
+      stage(smb[0]);
+      __syncthreads();
+      // the next chunk's gates, K, Q and V fly while this one computes
+      const bool more = c0 + kC < t_end;
+      pfn = 0;
+      pf_more = more;
+      pf_c0 = c0 + kC;
+      if (more) pf_gates(c0 + kC);
+      pf_next(2);
+      tiles(smb[0]);
+      __syncthreads();
+      part1(smb[0]);
+      part2(smb[0], c0);
+      if (more) prepare(c0 + kC);
+      __syncthreads();  // LDS reused by the next chunk
     }
-    if (more) prepare(c0 + kC);
-    __syncthreads();  // LDS reused by the next chunk
+  } else {
+    // period p: the producers prepare, stage and tile chunk p in buffer
+    // p & 1 and request chunk p + 1; the consumers run chunk p - 1 from
+    // buffer (p - 1) & 1.  Both sides pass the same two barriers per period.
+    const bool prod = w >= NW * HP;
+    const int nch = (t_end - t_begin + kC - 1) / kC;
+    for (int p = 0; nch > 0 && p <= nch; ++p) {
+      const int pc0 = t_begin + p * kC;
+      coords();
+      if (prod) {
+        if (p < nch) {
+          if (p > 0) prepare(pc0);
+          stage(smb[p & 1]);
+          if (p + 1 < nch) prefetch_all(pc0 + kC);
+        }
+      } else if (p > 0) {
+        part1(smb[(p - 1) & 1]);
+      }
+      __syncthreads();
+      if (prod) {
+        if (p < nch) tiles(smb[p & 1]);
+      } else if (p > 0) {
+        part2(smb[(p - 1) & 1], pc0 - kC);
+      }
+      __syncthreads();
+    }
   }
 
+  if (PC && w >= NW * HP) return;  // producers hold no state
   const float s_fin = ldexpf(1.0f, sexp);  // S = 2^E S_reg (exact)
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt)
@@ -927,20 +987,20 @@ __global__ __launch_bounds__(64 * NW * HP, NW * HP == 4 ? 2 : 1) void gdn_chunk_
       }
 }
 
-template <int D, typename TI, typename TO, int HP, int NW, int VS>
+template <int D, typename TI, typename TO, int HP, int NW, int VS, bool PC = false>
 hipError_t launch4(const GdnArgs& a, hipStream_t s) {
   const int units = a.n_seqs * (a.h_v / HP) * VS;
   const int per_xcd = (units + kXcd - 1) / kXcd;
-  dim3 grid(per_xcd * kXcd), block(64 * NW * HP);
+  dim3 grid(per_xcd * kXcd), block(64 * NW * HP * (PC ? 2 : 1));
   const bool o = a.o != nullptr;
   if (a.erase && o)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true, HP, NW, VS>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true, HP, NW, VS, PC>), grid, block, 0, s, a, per_xcd);
   else if (a.erase)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, false, HP, NW, VS>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, false, HP, NW, VS, PC>), grid, block, 0, s, a, per_xcd);
   else if (o)
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, true, HP, NW, VS>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, true, HP, NW, VS, PC>), grid, block, 0, s, a, per_xcd);
   else
-    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, false, HP, NW, VS>), grid, block, 0, s, a, per_xcd);
+    hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, false, false, HP, NW, VS, PC>), grid, block, 0, s, a, per_xcd);
   return hipGetLastError();
 }
 
@@ -948,9 +1008,14 @@ hipError_t launch4(const GdnArgs& a, hipStream_t s) {
 //  * two value heads per workgroup where the value heads of a key head pair
 //    up and there are at least two chains per compute unit;
 //  * at most half a chain per CU (d = 128): each chain's value columns split
-//    over two workgroups of 4 waves (the key-side tiles are formed by both),
-//    so the launch fills the CUs (4 x 32 chains: 118 instead of 128 us with
-//    outputs, 87 instead of 102 us state-only);
+//    over two workgroups (the key-side tiles are formed by both), so the
+//    launch fills the CUs (4 x 32 chains: 118 instead of 128 us with
+//    outputs, 87 instead of 102 us state-only).  Each workgroup is in the
+//    producer/consumer form: its 4 consumer waves (16 value columns each)
+//    run chunk c while 4 producer waves stage chunk c + 1 and form its tiles
+//    (4 x 32 chains: 95 instead of 111 us, 66 instead of 77 us state-only;
+//    the same form with one workgroup per chain, 32 columns per consumer
+//    wave, measured 3.7x slower at 8 x 32 chains);
 //  * up to one chain per CU (d = 128): one head of 8 waves (16 value columns
 //    per wave, two waves per SIMD); the two-workgroup split measured slower
 //    here (8 x 32 chains, scalar decay: 168 against 146 us);
@@ -960,7 +1025,7 @@ hipError_t launch3(const GdnArgs& a, hipStream_t s) {
   const int chains = a.n_seqs * a.h_v;
   if ((a.h_v / a.h_k) % 2 == 0 && chains >= 2 * kGfx950Cus) return launch4<D, TI, TO, 2, 4, 1>(a, s);
   if constexpr (D == 128) {  // 16 value columns per wave (d = 64 would leave 8)
-    if (2 * chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 4, 2>(a, s);
+    if (2 * chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 4, 2, true>(a, s);
     if (chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 8, 1>(a, s);
   }
   return launch4<D, TI, TO, 1, 4, 1>(a, s);
