@@ -430,27 +430,30 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
   }
 }
 
-// PC: producer/consumer form (one head, 4 consumer waves, VS = 2): 4 more
-// waves per workgroup stage chunk c + 1 and form its tiles while the 4
-// consumer waves run chunk c's state work, on two LDS buffers.
+// PC: producer/consumer form (one head of NW consumer waves): 4 more waves
+// per workgroup stage chunk c + 1 and form its tiles while the consumer
+// waves run chunk c's state work, on two LDS buffers.
+constexpr int kProducers = 4;  // producer waves of the PC form
 template <int D, typename TI, typename TO, bool ERASE, bool WANT_O, int HP, int NW, int VS, bool PC>
-__global__ __launch_bounds__(64 * NW * HP * (PC ? 2 : 1), NW * HP == 4 && !PC ? 2 : 1) void
+__global__ __launch_bounds__(64 * (NW * HP + (PC ? kProducers : 0)), NW * HP == 4 && !PC ? 2 : 1) void
 gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
-  static_assert(!PC || (HP == 1 && NW == 4), "the producer/consumer form has one head of 4 waves");
-  constexpr int kThreads = 64 * NW * HP;  // (consumer) waves' threads; as many producers in PC
+  static_assert(!PC || (HP == 1 && (NW == 4 || NW == 8)), "the producer/consumer form has one head");
+  constexpr int kThreads = 64 * NW * HP;  // the (consumer) waves' threads
+  // threads that load and stage the chunks: the producers in PC, else all
+  constexpr int kLoaders = PC ? 64 * kProducers : kThreads;
   constexpr int DV = D / VS;      // value columns of the workgroup (per head)
   constexpr int IW = DV / NW;     // value columns per wave
   constexpr int NIT = IW / 16;    // 16-wide column tiles per wave
   constexpr int NJT = D / 16;     // 16-wide key tiles
   constexpr int NKJ = D / 32;     // K = 32 steps over the key dimension
   constexpr int CPR = D / 8;      // 16-byte chunks per row
-  constexpr int NPF = kC * CPR / kThreads;  // 16-byte K (and Q) row pieces per thread
+  constexpr int NPF = kC * CPR / kLoaders;  // 16-byte K (and Q) row pieces per loader
   constexpr int VCPH = CPR / VS;            // 16-byte V pieces per token row and head
   constexpr int VCP = VCPH * HP;            // 16-byte V pieces per token row (all heads)
-  constexpr int NPFV = kC * VCP / kThreads; // V pieces per thread
+  constexpr int NPFV = kC * VCP / kLoaders; // V pieces per loader
   constexpr int kWS = ChunkSmem<D, HP>::kWS;
   static_assert(NIT >= 1 && IW % 16 == 0, "D too small");
-  static_assert(kC * CPR % kThreads == 0 && kThreads % VCP == 0,
+  static_assert(kC * CPR % kLoaders == 0 && kLoaders % VCP == 0,
                 "staging pieces must divide evenly");
 
   __shared__ ChunkSmem<D, HP> smb[PC ? 2 : 1];
@@ -538,23 +541,23 @@ gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
   // One 16-byte piece e of the next chunk's K, Q or V rows per thread (zero
   // past the end of the sequence), and the next chunk's gates (wave 0).
   auto pf_k = [&](int e, int c0n) {
-    const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
-    const uint16_t* kb = kg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
+    const int row = static_cast<int>(lane_row()) + (kLoaders / CPR) * e;
+    const uint16_t* kb = kg + static_cast<size_t>(c0n + (kLoaders / CPR) * e) * qk_row;
     pk[e] = u16x8{};
     if (row < t_end - c0n)
       pk[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(kb) + kq_off());
   };
   auto pf_q = [&](int e, int c0n) {
     if (!want_o) return;
-    const int row = static_cast<int>(lane_row()) + (kThreads / CPR) * e;
-    const uint16_t* qb = qg + static_cast<size_t>(c0n + (kThreads / CPR) * e) * qk_row;
+    const int row = static_cast<int>(lane_row()) + (kLoaders / CPR) * e;
+    const uint16_t* qb = qg + static_cast<size_t>(c0n + (kLoaders / CPR) * e) * qk_row;
     pq[e] = u16x8{};
     if (row < t_end - c0n)
       pq[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(qb) + kq_off());
   };
   auto pf_v = [&](int e, int c0n) {
-    const int row = static_cast<int>(v_lane_row()) + (kThreads / VCP) * e;
-    const uint16_t* vb = vg + static_cast<size_t>(c0n + (kThreads / VCP) * e) * v_row;
+    const int row = static_cast<int>(v_lane_row()) + (kLoaders / VCP) * e;
+    const uint16_t* vb = vg + static_cast<size_t>(c0n + (kLoaders / VCP) * e) * v_row;
     pv[e] = u16x8{};
     if (row < t_end - c0n)
       pv[e] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(vb) + v_off());
@@ -664,13 +667,13 @@ gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
       // ---- stage this chunk: K, Q, V rows (already fp16) and gate scalars --
 #pragma unroll
       for (int e = 0; e < NPF; ++e) {
-        const unsigned row = lane_row() + (kThreads / CPR) * e, col = lane_col();
+        const unsigned row = lane_row() + (kLoaders / CPR) * e, col = lane_col();
         lds_store16(lds_addr(sm.k) + 2 * (row * ChunkSmem<D, HP>::kKS + (col ^ kswz(row))), pk[e]);
         if (want_o) lds_store16(lds_addr(sm.q) + 2 * (row * ChunkSmem<D, HP>::kQS + col), pq[e]);
       }
 #pragma unroll
       for (int e = 0; e < NPFV; ++e) {
-        const unsigned row = v_lane_row() + (kThreads / VCP) * e, cp = v_lane_piece();
+        const unsigned row = v_lane_row() + (kLoaders / VCP) * e, cp = v_lane_piece();
         lds_store16(lds_addr(&sm.w[cp / VCPH][0]) + 2 * (row * kWS + col0 + 8 * (cp % VCPH)), pv[e]);
       }
       if (wq == 0) {
@@ -685,15 +688,25 @@ gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
       // Every wave forms the diagonal block of its head's rows 16 (w % 4)..
       // and inverts it (a wave-local LDS round trip, no barrier), and takes its
       // share of the off-diagonal A tiles and the P o QK^T tiles.
-      switch (PC ? w - NW * HP : w) {
-        case 0: chunk_tiles<D, HP, NW, ERASE, WANT_O, 0>(sm, lr, lg, a.scale); break;
-        case 1: chunk_tiles<D, HP, NW, ERASE, WANT_O, 1>(sm, lr, lg, a.scale); break;
-        case 2: chunk_tiles<D, HP, NW, ERASE, WANT_O, 2>(sm, lr, lg, a.scale); break;
-        case 3: chunk_tiles<D, HP, NW, ERASE, WANT_O, 3>(sm, lr, lg, a.scale); break;
-        case 4: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 4>(sm, lr, lg, a.scale); break;
-        case 5: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 5>(sm, lr, lg, a.scale); break;
-        case 6: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 6>(sm, lr, lg, a.scale); break;
-        default: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 7>(sm, lr, lg, a.scale); break;
+      if constexpr (PC) {
+        // the producers split the tile jobs as a 4-wave workgroup would
+        switch (w - NW * HP) {
+          case 0: chunk_tiles<D, HP, kProducers, ERASE, WANT_O, 0>(sm, lr, lg, a.scale); break;
+          case 1: chunk_tiles<D, HP, kProducers, ERASE, WANT_O, 1>(sm, lr, lg, a.scale); break;
+          case 2: chunk_tiles<D, HP, kProducers, ERASE, WANT_O, 2>(sm, lr, lg, a.scale); break;
+          default: chunk_tiles<D, HP, kProducers, ERASE, WANT_O, 3>(sm, lr, lg, a.scale); break;
+        }
+      } else {
+        switch (w) {
+          case 0: chunk_tiles<D, HP, NW, ERASE, WANT_O, 0>(sm, lr, lg, a.scale); break;
+          case 1: chunk_tiles<D, HP, NW, ERASE, WANT_O, 1>(sm, lr, lg, a.scale); break;
+          case 2: chunk_tiles<D, HP, NW, ERASE, WANT_O, 2>(sm, lr, lg, a.scale); break;
+          case 3: chunk_tiles<D, HP, NW, ERASE, WANT_O, 3>(sm, lr, lg, a.scale); break;
+          case 4: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 4>(sm, lr, lg, a.scale); break;
+          case 5: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 5>(sm, lr, lg, a.scale); break;
+          case 6: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 6>(sm, lr, lg, a.scale); break;
+          default: if constexpr (NW * HP == 8) chunk_tiles<D, HP, NW, ERASE, WANT_O, 7>(sm, lr, lg, a.scale); break;
+        }
       }
   };
   auto part1 = [&](ChunkSmem<D, HP>& sm) {
@@ -948,32 +961,35 @@ gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
   } else {
     // period p: the producers prepare, stage and tile chunk p in buffer
     // p & 1 and request chunk p + 1; the consumers run chunk p - 1 from
-    // buffer (p - 1) & 1.  Both sides pass the same two barriers per period.
-    const bool prod = w >= NW * HP;
+    // buffer (p - 1) & 1.  Each side has its own loop (so neither holds the
+    // other's registers: the state, the prefetched rows), and both pass the
+    // same two barriers per period.
     const int nch = (t_end - t_begin + kC - 1) / kC;
-    for (int p = 0; nch > 0 && p <= nch; ++p) {
-      const int pc0 = t_begin + p * kC;
-      coords();
-      if (prod) {
+    if (w >= NW * HP) {
+      for (int p = 0; nch > 0 && p <= nch; ++p) {
+        const int pc0 = t_begin + p * kC;
+        coords();
         if (p < nch) {
           if (p > 0) prepare(pc0);
           stage(smb[p & 1]);
           if (p + 1 < nch) prefetch_all(pc0 + kC);
         }
-      } else if (p > 0) {
-        part1(smb[(p - 1) & 1]);
-      }
-      __syncthreads();
-      if (prod) {
+        __syncthreads();
         if (p < nch) tiles(smb[p & 1]);
-      } else if (p > 0) {
-        part2(smb[(p - 1) & 1], pc0 - kC);
+        __syncthreads();
       }
+      return;  // producers hold no state
+    }
+    for (int p = 0; nch > 0 && p <= nch; ++p) {
+      const int pc0 = t_begin + p * kC;
+      coords();
+      if (p > 0) part1(smb[(p - 1) & 1]);
+      __syncthreads();
+      if (p > 0) part2(smb[(p - 1) & 1], pc0 - kC);
       __syncthreads();
     }
   }
 
-  if (PC && w >= NW * HP) return;  // producers hold no state
   const float s_fin = ldexpf(1.0f, sexp);  // S = 2^E S_reg (exact)
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt)
@@ -991,7 +1007,7 @@ template <int D, typename TI, typename TO, int HP, int NW, int VS, bool PC = fal
 hipError_t launch4(const GdnArgs& a, hipStream_t s) {
   const int units = a.n_seqs * (a.h_v / HP) * VS;
   const int per_xcd = (units + kXcd - 1) / kXcd;
-  dim3 grid(per_xcd * kXcd), block(64 * NW * HP * (PC ? 2 : 1));
+  dim3 grid(per_xcd * kXcd), block(64 * (NW * HP + (PC ? kProducers : 0)));
   const bool o = a.o != nullptr;
   if (a.erase && o)
     hipLaunchKernelGGL((gdn_chunk_kernel<D, TI, TO, true, true, HP, NW, VS, PC>), grid, block, 0, s, a, per_xcd);
@@ -1013,12 +1029,13 @@ hipError_t launch4(const GdnArgs& a, hipStream_t s) {
 //    outputs, 87 instead of 102 us state-only).  Each workgroup is in the
 //    producer/consumer form: its 4 consumer waves (16 value columns each)
 //    run chunk c while 4 producer waves stage chunk c + 1 and form its tiles
-//    (4 x 32 chains: 95 instead of 111 us, 66 instead of 77 us state-only;
+//    (4 x 32 chains: 86 instead of 111 us, 57 instead of 77 us state-only;
 //    the same form with one workgroup per chain, 32 columns per consumer
 //    wave, measured 3.7x slower at 8 x 32 chains);
-//  * up to one chain per CU (d = 128): one head of 8 waves (16 value columns
-//    per wave, two waves per SIMD); the two-workgroup split measured slower
-//    here (8 x 32 chains, scalar decay: 168 against 146 us);
+//  * up to one chain per CU (d = 128): the producer/consumer form with 8
+//    consumer waves (16 value columns each, two per SIMD) and 4 producer
+//    waves (8 x 32 chains without erasure: 139 against 144 us for 8 plain
+//    waves; the two-workgroup split measured 168 us there);
 //  * otherwise one head of 4 waves.
 template <int D, typename TI, typename TO>
 hipError_t launch3(const GdnArgs& a, hipStream_t s) {
@@ -1026,7 +1043,7 @@ hipError_t launch3(const GdnArgs& a, hipStream_t s) {
   if ((a.h_v / a.h_k) % 2 == 0 && chains >= 2 * kGfx950Cus) return launch4<D, TI, TO, 2, 4, 1>(a, s);
   if constexpr (D == 128) {  // 16 value columns per wave (d = 64 would leave 8)
     if (2 * chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 4, 2, true>(a, s);
-    if (chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 8, 1>(a, s);
+    if (chains <= kGfx950Cus) return launch4<D, TI, TO, 1, 8, 1, true>(a, s);
   }
   return launch4<D, TI, TO, 1, 4, 1>(a, s);
 }
