@@ -119,6 +119,16 @@ __device__ __forceinline__ constexpr int kperm(int c) {
   return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c & 31) >> 4) + (c & 3);
 }
 
+// Four consecutive columns 4m..4m+3 land on four consecutive, 8-byte aligned
+// storage positions (the tile epilogue stores them with one 8-byte write).
+__device__ __forceinline__ constexpr bool kperm_quads_contiguous() {
+  for (int c = 0; c < kC; c += 4)
+    for (int r = 0; r < 4; ++r)
+      if (kperm(c + r) != kperm(c) + r || kperm(c) % 4 != 0) return false;
+  return kAS % 4 == 0 && kPS % 4 == 0;
+}
+static_assert(kperm_quads_contiguous(), "tile stores need column quads contiguous");
+
 // Column swizzle of K row t (fp16 elements, XORed into the column): rows
 // 4..7 of every 8 exchange their 16-byte column chunks pairwise.
 __device__ __forceinline__ int kswz(int t) { return 8 * ((t >> 2) & 1); }
@@ -288,33 +298,41 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
   f32x4 acc[NS];
 #pragma unroll
   for (int q = 0; q < NS; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Element layout: the diagonal block (slot 0) stays in the accumulator
+  // layout the inverse works in (lane (lr, lg) holds rows 16tr+4lg+r of column
+  // 16tc+lr).  The other tiles are formed transposed (operands swapped, the
+  // same products), so lane (lr, lg) holds row 16tr+lr at the 4 consecutive
+  // columns 16tc+4lg+r, which sit next to each other in the kperm storage
+  // order: one 8-byte LDS store per tile and head.
+  auto el_row = [=](int q, int r) { return q == 0 ? 16 * slot_tr(q) + 4 * lg + r : 16 * slot_tr(q) + lr; };
+  auto el_col = [=](int q, int r) { return q == 0 ? 16 * slot_tc(q) + lr : 16 * slot_tc(q) + 4 * lg + r; };
   // decay / gate factors of this lane's tile elements, formed before the
   // products (they do not depend on them): masked b_t e^{G_t-G_j} for the
   // diagonal A block, -e^{G_t-G_j} for the others (-A~), scale e^{G_t-G_j}
-  // for P o QK^T.  The gate values are read unconditionally (four rows per
-  // vector read) and the causal mask applied by selects, so no LDS read sits
-  // behind a branch.
+  // for P o QK^T.  The gate values are read unconditionally (four rows or
+  // columns per vector read) and the causal mask applied by selects, so no
+  // LDS read sits behind a branch.
   float f[NS][HP][4];
 #pragma unroll
   for (int q = 0; q < NS; ++q) {
     if (!slot_on(q)) continue;
-    const int col = 16 * slot_tc(q) + lr;
-    const int row0 = 16 * slot_tr(q) + 4 * lg;
 #pragma unroll
     for (int hh = 0; hh < slot_nh(q); ++hh) {
       const int hd = slot_h0(q) + hh;
-      const float gcol = sm.gcum[hd][col];
-      const f32x4 grow = *reinterpret_cast<const f32x4*>(&sm.gcum[hd][row0]);
+      // the lane's scalar (column for slot 0, row otherwise) and its 4-vector
+      const float g1 = sm.gcum[hd][q == 0 ? el_col(q, 0) : el_row(q, 0)];
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sm.gcum[hd][q == 0 ? el_row(q, 0) : el_col(q, 0)]);
       // b_t only on the diagonal block (the inverse needs the true A_bb); the
       // off-diagonal A tiles hold -A~, the P o QK^T tiles carry the scale
-      const f32x4 wrow = q == 0 ? *reinterpret_cast<const f32x4*>(&sm.beta[hd][row0])
+      const f32x4 wrow = q == 0 ? *reinterpret_cast<const f32x4*>(&sm.beta[hd][el_row(q, 0)])
                          : slot_kk(q) ? f32x4{1.0f, 1.0f, 1.0f, 1.0f}
                                       : f32x4{scale, scale, scale, scale};
       const float sgn = (q == 0 || !slot_kk(q)) ? 1.0f : -1.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = row0 + r;
-        const float v = sgn * wrow[r] * __builtin_amdgcn_exp2f(grow[r] - gcol);
+        const int row = el_row(q, r), col = el_col(q, r);
+        const float gd = q == 0 ? g4[r] - g1 : g1 - g4[r];  // G_row - G_col
+        const float v = sgn * wrow[r] * __builtin_amdgcn_exp2f(gd);
         const bool keep = slot_kk(q) ? row > col : row >= col;
         f[q][hh][r] = keep ? v : 0.0f;
       }
@@ -332,7 +350,7 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
       const f16x8 av = slot_kk(q) ? lds8_at(kl, 2 * kidx<D>(16 * slot_tr(q), 32 * ks))
                                   : lds8_at(ql, 2 * qidx<D>(16 * slot_tr(q), 32 * ks));
       const f16x8 bv = lds8_at(kl, 2 * kidx<D>(16 * slot_tc(q), 32 * ks));
-      acc[q] = mfma16x16x32(av, bv, acc[q]);
+      acc[q] = q == 0 ? mfma16x16x32(av, bv, acc[q]) : mfma16x16x32(bv, av, acc[q]);
     }
   }
   tr_keep(kl);
@@ -343,20 +361,19 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
 #pragma unroll
   for (int q = 0; q < NS; ++q) {
     if (!slot_on(q)) continue;
-    const int col = 16 * slot_tc(q) + lr;
 #pragma unroll
     for (int hh = 0; hh < slot_nh(q); ++hh) {
       const int hd = slot_h0(q) + hh;
+      if (q == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * slot_tr(q) + 4 * lg + r;
-        const float val = f[q][hh][r] * acc[q][r];
-        if (q == 0)
-          nd[r] = val;
-        else if (slot_kk(q))
-          sm.a[hd][row * kAS + kperm(col)] = static_cast<_Float16>(val);
-        else
-          sm.pqk[hd][row * kPS + kperm(col)] = static_cast<_Float16>(val);
+        for (int r = 0; r < 4; ++r) nd[r] = f[q][hh][r] * acc[q][r];
+      } else {
+        f16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = static_cast<_Float16>(f[q][hh][r] * acc[q][r]);
+        _Float16* dst = slot_kk(q) ? &sm.a[hd][el_row(q, 0) * kAS + kperm(el_col(q, 0))]
+                                   : &sm.pqk[hd][el_row(q, 0) * kPS + kperm(el_col(q, 0))];
+        *reinterpret_cast<f16x4*>(dst) = o;
       }
     }
   }
