@@ -102,10 +102,12 @@ def test_value_head_pairs(d, hk, erase):
 def test_launch_shapes(n_seqs, hk, hv, erase):
     """The launch picks its workgroup shape from the number of (sequence,
     value head) chains: 512 chains with one value head per key head and 384
-    chains take one head of 4 waves per workgroup, 256 chains one head of 8
-    waves, 128 chains two workgroups of 4 waves per chain (value columns
-    split; pairs of heads are covered above).  Full parity with ragged
-    lengths and an initial state, and state-only equals the full run."""
+    chains take one head of 4 waves per workgroup; 256 chains one head of 8
+    consumer waves beside 4 producer waves (which stage and tile the next
+    chunk); 128 chains two workgroups per chain (value columns split), each
+    4 consumer and 4 producer waves (pairs of heads are covered above).  Full
+    parity with ragged lengths and an initial state, and state-only equals
+    the full run."""
     lens = (PAIR_LENS * 2)[:n_seqs]
     c = gdn_case(lens, hk, hv, 128, "bf16", seed=7 * n_seqs + hk + int(erase), normalize_q=True,
                  erase=erase, initial_state=True)
@@ -295,8 +297,8 @@ def test_full_size_every_sequence(which):
 def test_packed_equals_solo_across_launch_shapes(n_seqs):
     """16 sequences x 32 value heads (512 chains: value-head pairs per
     workgroup), 9 x 32 (288 chains: one head of 4 waves) and 8 x 32 (256
-    chains: one head of 8 waves) against each sequence replayed alone (32
-    chains: two workgroups of 4 waves per chain): bit-identical states and
+    chains: 8 consumer and 4 producer waves) against each sequence replayed
+    alone (32 chains: two producer/consumer workgroups per chain): bit-identical states and
     outputs, so no result depends on the launch shape or on a sequence's
     neighbours."""
     lens = (PAIR_LENS * 2)[:n_seqs]
