@@ -52,16 +52,17 @@ namespace {
 
 constexpr int kC = 64;         // chunk length (tokens)
 // A workgroup holds HP value heads that share one key head, with NW waves
-// per head (HP x NW = 4 or 8 waves):
+// per head (HP x NW = 4 or 8 waves), plus 4 producer waves in the
+// producer/consumer form (PC), which stage the next chunk and form its
+// tiles while the NW consumer waves run the current one:
 //  * HP = 2, NW = 4 where the value heads per key head are even and there
 //    are at least two (sequence, head) chains per CU: K and Q rows are
 //    loaded and staged once and the raw K K^T / Q K^T tiles formed once for
 //    both heads; one workgroup of 8 waves per CU;
-//  * HP = 1, NW = 8 for at most one chain per CU: 16 value columns per
-//    wave, two waves per SIMD instead of one;
-//  * HP = 1, NW = 4, VS = 2 for at most half a chain per CU: two workgroups
-//    per chain, 16 value columns per wave, plus 4 producer waves per
-//    workgroup (PC) that stage the next chunk and form its tiles;
+//  * HP = 1, NW = 8, PC for at most one chain per CU: 16 value columns per
+//    consumer wave, 12 waves (three per SIMD);
+//  * HP = 1, NW = 4, VS = 2, PC for at most half a chain per CU: two
+//    workgroups per chain, 16 value columns per consumer wave;
 //  * HP = 1, NW = 4 otherwise: two workgroups of 4 waves per CU.
 constexpr int kAS = kC + 8;    // fp16 row stride of -A
 constexpr int kPS = kC + 8;    // fp16 row stride of P o QK^T
