@@ -439,6 +439,33 @@ __device__ __forceinline__ void gemm_mainloop(const _Float16* __restrict__ A, in
   }
 }
 
+// Epilogue of four consecutive results C[m][n..n+3] (n % 4 == 0), shared by
+// every GEMM kernel so that all of them apply the same arithmetic.
+template <int EPI>
+__device__ __forceinline__ void gemm_store4(void* C, int ldc, const void* X, int ldx, int m, int n,
+                                            f32x4 v) {
+  const size_t ci = static_cast<size_t>(m) * ldc + n;
+  if (EPI == EPI_STORE16) {
+    *reinterpret_cast<f16x4*>(static_cast<_Float16*>(C) + ci) = to_f16x4(v);
+  } else if (EPI == EPI_SWIGLU) {
+    const f16x2 h = {static_cast<_Float16>(silu(v[0]) * v[1]),
+                     static_cast<_Float16>(silu(v[2]) * v[3])};
+    *reinterpret_cast<f16x2*>(static_cast<_Float16*>(C) + static_cast<size_t>(m) * ldc + n / 2) = h;
+  } else if (EPI == EPI_ADD_F32 || EPI == EPI_ADD_BF16) {
+    const size_t xi = static_cast<size_t>(m) * ldx + n;
+    f32x4 x;
+    if (EPI == EPI_ADD_F32) {
+      x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(X) + xi);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = load1<BF16>(X, xi + e);
+    }
+    *reinterpret_cast<f32x4*>(static_cast<float*>(C) + ci) = x + v;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(C) + ci) = v;
+  }
+}
+
 // Tiles q_begin .. q_begin + q_count - 1 of the grouped order: one per
 // workgroup (NJ = 4), or one 64-column strip per workgroup (NJ = 1).
 template <int EPI, int NJ>
@@ -485,28 +512,68 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const _Float16* __restrict
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * 32 * NJ + 32 * j + 8 * g + 4 * (l / 32);
         if (n >= N) continue;  // N % 4 == 0: a group of 4 is in or out as a whole
-        const size_t ci = static_cast<size_t>(m) * ldc + n;
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        if (EPI == EPI_STORE16) {
-          *reinterpret_cast<f16x4*>(static_cast<_Float16*>(C) + ci) = to_f16x4(v);
-        } else if (EPI == EPI_SWIGLU) {
-          const f16x2 h = {static_cast<_Float16>(silu(v[0]) * v[1]),
-                           static_cast<_Float16>(silu(v[2]) * v[3])};
-          *reinterpret_cast<f16x2*>(static_cast<_Float16*>(C) + static_cast<size_t>(m) * ldc + n / 2) = h;
-        } else if (EPI == EPI_ADD_F32 || EPI == EPI_ADD_BF16) {
-          const size_t xi = static_cast<size_t>(m) * ldx + n;
-          f32x4 x;
-          if (EPI == EPI_ADD_F32) {
-            x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(X) + xi);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = load1<BF16>(X, xi + e);
-          }
-          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + ci) = x + v;
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + ci) = v;
-        }
+        gemm_store4<EPI>(C, ldc, X, ldx, m, n, v);
       }
+  }
+}
+
+// A few tiles left over after the full rounds, as 32 x 32 blocks of C, one
+// wave each: tile q_begin + b/64 of the grouped order, block (b%64)/8 of its
+// rows and b%8 of its columns.  A handful of leftover tiles then spreads
+// over the CUs instead of holding a few of them for a whole tile time.  The
+// operands come straight from global memory (16-byte pieces, PF k-steps in
+// flight); each element is accumulated by the same MFMA, with the B fragment
+// first, over the same k order as in gemm_kernel, in one accumulation chain,
+// so results do not depend on which kernel computed them.
+template <int EPI>
+__global__ __launch_bounds__(64) void gemm_block_kernel(const _Float16* __restrict__ A, int lda,
+                                                        const _Float16* __restrict__ Bt, int ldb,
+                                                        int M, int N, int K, void* C, int ldc,
+                                                        const void* X, int ldx, int q_begin) {
+  const int l = threadIdx.x;
+  const int b = blockIdx.x;
+  int tm, tn;
+  gemm_tile_at(q_begin + b / 64, (M + GBM - 1) / GBM, (N + GBN - 1) / GBN, tm, tn);
+  const int m0 = tm * GBM + 32 * ((b % 64) / 8);
+  const int n0 = tn * GBN + 32 * (b % 8);
+  if (m0 >= M || n0 >= N) return;
+  // lane l: row l%32 of the A and Bt blocks (clamped into range: computed,
+  // never stored), k 8(l/32)..+7 of each k16 step; 32-bit byte offsets from
+  // a uniform base, as in gemm_kernel
+  const uint32_t ao = static_cast<uint32_t>(
+      (static_cast<size_t>(min(m0 + l % 32, M - 1)) * lda + 8 * (l / 32)) * 2);
+  const uint32_t bo = static_cast<uint32_t>(
+      (static_cast<size_t>(min(n0 + l % 32, N - 1)) * ldb + 8 * (l / 32)) * 2);
+  const int ns = K / 16;  // k16 steps
+  constexpr int PF = 16;  // steps in flight
+  f16x8 ar[PF], br[PF];
+  auto load = [&](int p, int step) {
+    const int k0 = 16 * min(step, ns - 1);  // past the end: reload the last step (never used)
+    ar[p] = *reinterpret_cast<const f16x8*>(reinterpret_cast<const char*>(A + k0) + ao);
+    br[p] = *reinterpret_cast<const f16x8*>(reinterpret_cast<const char*>(Bt + k0) + bo);
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load(p, p);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      if (s0 + p < ns) acc = mfma32x32x16(br[p], ar[p], acc);
+      load(p, s0 + p + PF);
+    }
+  }
+  // lane l: row m0 + l%32; register group g: columns n0 + 8g + 4(l/32) .. +3
+  const int m = m0 + l % 32;
+  if (m >= M) return;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int n = n0 + 8 * g + 4 * (l / 32);
+    if (n >= N) continue;  // N % 4 == 0: a group of 4 is in or out as a whole
+    const f32x4 v = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+    gemm_store4<EPI>(C, ldc, X, ldx, m, n, v);
   }
 }
 
@@ -966,9 +1033,15 @@ hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, 
     // whole A panel, and measures about half a tile's time (260 tiles of the
     // 6552 x 2560 x 4096 output projection: 205 us as two rounds, 124 + 61 us
     // with the last 4 tiles as 16 strips).
-    int full = tiles, narrow = 0;
+    // Up to 16 leftover tiles go out as 32 x 32 blocks instead (one wave
+    // each, at most 4 per CU): the 4 leftover tiles of that projection as
+    // 16 strips take ~59 us on 16 CUs.
+    int full = tiles, narrow = 0, blocks = 0;
     const int rest = tiles % kGfx950Cus;
-    if (rest != 0 && kStrips * rest <= kGfx950Cus) {
+    if (rest != 0 && 64 * rest <= 4 * kGfx950Cus) {
+      full = tiles - rest;
+      blocks = rest;
+    } else if (rest != 0 && kStrips * rest <= kGfx950Cus) {
       full = tiles - rest;
       narrow = rest;
     }
@@ -984,6 +1057,13 @@ hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, 
       dim3 grid((full + kXcdG - 1) / kXcdG * kXcdG), block(256);
       hipLaunchKernelGGL((gemm_kernel<EPI, 4>), grid, block, 0, s, Am, lda, Bt, ldb, mm, N, K, Cm,
                          ldc, Xm, ldx, 0, full);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (blocks > 0) {
+      dim3 grid(blocks * 64), block(64);
+      hipLaunchKernelGGL((gemm_block_kernel<EPI>), grid, block, 0, s, Am, lda, Bt, ldb, mm, N, K, Cm,
+                         ldc, Xm, ldx, full);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
