@@ -546,7 +546,7 @@ __global__ __launch_bounds__(64) void gemm_block_kernel(const _Float16* __restri
   const uint32_t bo = static_cast<uint32_t>(
       (static_cast<size_t>(min(n0 + l % 32, N - 1)) * ldb + 8 * (l / 32)) * 2);
   const int ns = K / 16;  // k16 steps
-  constexpr int PF = 16;  // steps in flight
+  constexpr int PF = 32;  // steps in flight
   f16x8 ar[PF], br[PF];
   auto load = [&](int p, int step) {
     const int k0 = 16 * min(step, ns - 1);  // past the end: reload the last step (never used)
