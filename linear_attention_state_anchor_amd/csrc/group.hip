@@ -211,12 +211,13 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const void* x, int rows, 
 // Tile order: workgroups are dealt round-robin to the 8 XCDs, so each XCD is
 // given a contiguous range of a grouped order (8 M-tiles wide, walking N):
 // the ~32 tiles an XCD runs at a time share 8 A and 4 B panels in its L2.
-// Narrow variant (NJ = 1): the same tile split into four 256 x 64 strips, one
-// per workgroup (4 waves of 128 x 32), for the tiles of a last, partly
-// filled round: a launch of 260 tiles on 256 CUs would otherwise take two
-// full tile times.  Every output element is accumulated by the same MFMA
-// sequence over the same k order in both variants, so results do not depend
-// on which variant computed them.
+// Leftover tiles of a last, partly filled round (a launch of 260 tiles on
+// 256 CUs would otherwise take two full tile times): up to 16 of them run
+// as 32 x 32 blocks, one wave each (gemm_block_kernel); more, up to 64, in
+// the narrow variant (NJ = 1): the tile split into four 256 x 64 strips, one
+// per workgroup (4 waves of 128 x 32).  Every output element is accumulated
+// by the same MFMA sequence over the same k order in all of them, so results
+// do not depend on which kernel computed them.
 // Requirements: K % 64 == 0, N % 4 == 0, lda/ldb/ldc multiples of 8; M and
 // N are guarded.
 // ---------------------------------------------------------------------------
