@@ -452,6 +452,14 @@ __device__ __forceinline__ void chunk_tiles(ChunkSmem<D, HP>& sm, int lr, int lg
 // per workgroup stage chunk c + 1 and form its tiles while the consumer
 // waves run chunk c's state work, on two LDS buffers.
 constexpr int kProducers = 4;  // producer waves of the PC form
+// Launches that order their chains longest first: the plain forms (the
+// producer/consumer forms run at most one chain per CU at a time) of 2 to
+// kLptMax sequences (each workgroup ranks them all).
+constexpr int kLptMax = 256;
+template <bool PC>
+__host__ __device__ constexpr bool lpt_launch(int n_seqs) {
+  return !PC && n_seqs >= 2 && n_seqs <= kLptMax;
+}
 template <int D, typename TI, typename TO, bool ERASE, bool WANT_O, int HP, int NW, int VS, bool PC>
 __global__ __launch_bounds__(64 * (NW * HP + (PC ? kProducers : 0)), NW * HP == 4 && !PC ? 2 : 1) void
 gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
@@ -481,14 +489,44 @@ gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
   // read K and Q through one L2).
   // (with VS > 1 the VS column slices of one chain are consecutive units, so
   // they share an XCD and read the chain's K and Q through one L2)
-  const int unit = (blockIdx.x % kXcd) * units_per_xcd + blockIdx.x / kXcd;
   const int groups = a.h_v / HP;  // head groups per sequence
-  if (unit >= a.n_seqs * groups * VS) return;  // padding workgroup
-  const int n = unit / (groups * VS);
-  const int hb = ((unit / VS) % groups) * HP;  // first value head of the workgroup
-  const int col0 = (unit % VS) * DV;           // first value column of the workgroup
-  const int g = hb / (a.h_v / a.h_k);
   const int tid = threadIdx.x;
+  int n, hgrp, slice;  // sequence, head group and column slice of the workgroup
+  if (lpt_launch<PC>(a.n_seqs)) {
+    // Longest chains first: every workgroup ranks the sequences by length
+    // (descending, ties by index), and XCD x runs the sequences of ranks
+    // x, x + 8, x + 16, ... in that order with all head groups of a
+    // sequence in a row.  A ragged batch then does not end with a few long
+    // chains on a few CUs; each chain's arithmetic is unchanged.
+    __shared__ int lpt_len[kLptMax], lpt_seq[kLptMax];
+    for (int e = tid; e < a.n_seqs; e += blockDim.x) lpt_len[e] = a.cu[e + 1] - a.cu[e];
+    __syncthreads();
+    for (int e = tid; e < a.n_seqs; e += blockDim.x) {
+      const int le = lpt_len[e];
+      int r = 0;
+      for (int t = 0; t < a.n_seqs; ++t) {
+        const int lt = lpt_len[t];
+        r += (lt > le || (lt == le && t < e)) ? 1 : 0;
+      }
+      lpt_seq[r] = e;
+    }
+    __syncthreads();
+    const int j = blockIdx.x / kXcd;
+    const int rho = kXcd * (j / groups) + static_cast<int>(blockIdx.x % kXcd);
+    if (rho >= a.n_seqs) return;  // padding workgroup
+    n = lpt_seq[rho];
+    hgrp = j % groups;
+    slice = 0;
+  } else {
+    const int unit = (blockIdx.x % kXcd) * units_per_xcd + blockIdx.x / kXcd;
+    if (unit >= a.n_seqs * groups * VS) return;  // padding workgroup
+    n = unit / (groups * VS);
+    hgrp = (unit / VS) % groups;
+    slice = unit % VS;
+  }
+  const int hb = hgrp * HP;     // first value head of the workgroup
+  const int col0 = slice * DV;  // first value column of the workgroup
+  const int g = hb / (a.h_v / a.h_k);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int hp = PC ? 0 : w / NW;  // this wave's head within the workgroup
   const int wq = w % NW;  // this wave within its head
@@ -1024,7 +1062,12 @@ gdn_chunk_kernel(GdnArgs a, int units_per_xcd) {
 template <int D, typename TI, typename TO, int HP, int NW, int VS, bool PC = false>
 hipError_t launch4(const GdnArgs& a, hipStream_t s) {
   const int units = a.n_seqs * (a.h_v / HP) * VS;
-  const int per_xcd = (units + kXcd - 1) / kXcd;
+  int per_xcd = (units + kXcd - 1) / kXcd;
+  // longest-first order: XCD x takes the sequences of ranks x, x + 8, ...
+  if (lpt_launch<PC>(a.n_seqs)) {
+    const int lpt_per_xcd = (a.h_v / HP) * ((a.n_seqs + kXcd - 1) / kXcd);
+    if (lpt_per_xcd > per_xcd) per_xcd = lpt_per_xcd;
+  }
   dim3 grid(per_xcd * kXcd), block(64 * (NW * HP + (PC ? kProducers : 0)));
   const bool o = a.o != nullptr;
   if (a.erase && o)
