@@ -1029,14 +1029,13 @@ hipError_t gemm(const _Float16* A, int lda, const _Float16* Bt, int ldb, int M, 
     const int mm = std::min(mc, M - m_at);
     const int tiles = ((N + GBN - 1) / GBN) * ((mm + GBM - 1) / GBM);
     // Full rounds of whole tiles on the CUs; the tiles of a last, partly
-    // filled round go out as 64-column strips when their strips fit in one
-    // round: a strip does a quarter of a tile's MFMAs but still streams the
-    // whole A panel, and measures about half a tile's time (260 tiles of the
-    // 6552 x 2560 x 4096 output projection: 205 us as two rounds, 124 + 61 us
-    // with the last 4 tiles as 16 strips).
-    // Up to 16 leftover tiles go out as 32 x 32 blocks instead (one wave
-    // each, at most 4 per CU): the 4 leftover tiles of that projection as
-    // 16 strips take ~59 us on 16 CUs.
+    // filled round go out as 32 x 32 blocks (up to 16 tiles: one wave per
+    // block, at most 4 blocks per CU) or as 64-column strips (up to 64
+    // tiles: their strips fit in one round).  A strip does a quarter of a
+    // tile's MFMAs but still streams the whole A panel and takes about half
+    // a tile's time.  The 260 tiles of the 6552 x 2560 x 4096 output
+    // projection: 205 us as two rounds, 124 + 61 us with the last 4 tiles as
+    // 16 strips on 16 CUs, ~144 + 22 us with them as 160 blocks.
     int full = tiles, narrow = 0, blocks = 0;
     const int rest = tiles % kGfx950Cus;
     if (rest != 0 && 64 * rest <= 4 * kGfx950Cus) {
