@@ -725,18 +725,28 @@ __global__ __launch_bounds__(256) void frontend_kernel(
 // in the tile.  Every value is computed exactly as gemm_kernel<EPI_STORE16>
 // followed by frontend_kernel computes it (same fp16 rounding, tap order,
 // SiLU and L2 sum).  A lane owns 8 adjacent columns of the tile and walks 32
-// rows, four at a time.  The a|b columns go to P like z; gates_kernel
+// rows (16 in a half tile), four at a time.  The a|b columns go to P like z; gates_kernel
 // forms the gates from them.
 // ---------------------------------------------------------------------------
 constexpr int FTM = GBM - 3;   // rows emitted per tile
 constexpr int FTS = GBN + 8;   // row stride (halves) of the staged tile
 
-template <int D>
+// NJF = 4: whole 256-column tiles q_begin .. q_begin + q_count - 1 of the
+// grouped order; NJF = 2: the same tiles as two 128-column halves each (one
+// per workgroup; a half holds whole heads), for the tiles of a last, partly
+// filled round when their halves fit in one round.  Each element is
+// accumulated and finished exactly as in a whole tile.
+template <int D, int NJF>
 __global__ __launch_bounds__(256, 1) void gemm_front_kernel(
     const _Float16* __restrict__ A, int lda, const _Float16* __restrict__ Bt, int ldb, int M,
     int N, int K, LayerShape L, const float* __restrict__ convw,
     const int32_t* __restrict__ seq_start, float l2_eps, _Float16* __restrict__ P, int ldp,
-    _Float16* __restrict__ qo, _Float16* __restrict__ ko, _Float16* __restrict__ vo) {
+    _Float16* __restrict__ qo, _Float16* __restrict__ ko, _Float16* __restrict__ vo, int q_begin,
+    int q_count) {
+  static_assert(NJF == 4 || NJF == 2, "whole tiles or halves");
+  constexpr int BNF = 64 * NJF;     // columns of the workgroup
+  constexpr int LPR = BNF / 8;      // lanes per tile row in the front end (8 columns each)
+  constexpr int RPG = GBM * LPR / 256;  // rows walked by each lane group
   __shared__ _Float16 sm[2 * (GBM * GLD + GBN * GLD)];
   __shared__ int sst[GBM];
   static_assert(GBM * FTS <= 2 * (GBM * GLD + GBN * GLD), "staged tile must fit the LDS buffers");
@@ -745,18 +755,25 @@ __global__ __launch_bounds__(256, 1) void gemm_front_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l = tid % kWave;
   const int wm = w / 2, wn = w % 2;
-  int tm, tn;
+  int tm, tn, half = 0;
   {
     const int n_m = (M + FTM - 1) / FTM, n_n = (N + GBN - 1) / GBN;
-    const int tiles = n_m * n_n, per_xcd = (tiles + kXcdG - 1) / kXcdG;
-    const int q = (blockIdx.x % kXcdG) * per_xcd + blockIdx.x / kXcdG;
-    if (q >= tiles) return;
-    gemm_tile_at(q, n_m, n_n, tm, tn);
+    int q;
+    if (NJF == 4) {
+      const int per_xcd = (q_count + kXcdG - 1) / kXcdG;
+      q = (blockIdx.x % kXcdG) * per_xcd + blockIdx.x / kXcdG;
+    } else {
+      q = blockIdx.x / 2;
+      half = blockIdx.x % 2;
+    }
+    if (q >= q_count) return;
+    gemm_tile_at(q_begin + q, n_m, n_n, tm, tn);
   }
-  const int n0 = tn * GBN;
+  const int n0 = tn * GBN + BNF * half;
+  if (n0 >= N) return;  // a half past the last column
   const int m0 = tm * FTM - 3;
-  f32x16 acc[4][4];
-  gemm_mainloop<4>(A, lda, Bt, ldb, M, N, K, m0, n0, sm, acc);
+  f32x16 acc[4][NJF];
+  gemm_mainloop<NJF>(A, lda, Bt, ldb, M, N, K, m0, n0, sm, acc);
   // (the main loop ends with a barrier: its LDS buffers are free)
   {
     const int t = m0 + tid;
@@ -766,18 +783,18 @@ __global__ __launch_bounds__(256, 1) void gemm_front_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJF; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row = wm * 128 + 32 * i + l % 32;
-        const int col = wn * 128 + 32 * j + 8 * g + 4 * (l / 32);
+        const int col = wn * 32 * NJF + 32 * j + 8 * g + 4 * (l / 32);
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         *reinterpret_cast<f16x4*>(T16 + row * FTS + col) = to_f16x4(v);
       }
   __syncthreads();
 
   // this lane's 8 columns and what they are
-  const int cb = l % 32;
+  const int cb = l % LPR;
   const int col = n0 + 8 * cb;
   const int hk = L.h_k, hv = L.h_v;
   int kind = -1, hidx = 0, nh = 1, cin = 0;  // 0 k, 1 v, 2 q, 3 gates, 4 z
@@ -804,9 +821,9 @@ __global__ __launch_bounds__(256, 1) void gemm_front_kernel(
 #pragma unroll
     for (int k = 0; k < 4; ++k) wt[e][k] = conv && k < W ? convw[(ch0 + e) * W + (W - 1 - k)] : 0.0f;
 
-  const int r0 = 3 + 32 * (w * 2 + l / 32), r1 = min(r0 + 32, GBM);
+  const int r0 = 3 + RPG * (w * (kWave / LPR) + l / LPR), r1 = min(r0 + RPG, GBM);
   // tiles without conv columns (z, pad) only copy z (and a|b) to P
-  const bool any_conv = n0 < L.n_kv() || (n0 < L.q_off() + hk * D && n0 + GBN > L.q_off());
+  const bool any_conv = n0 < L.n_kv() || (n0 < L.q_off() + hk * D && n0 + BNF > L.q_off());
   if (!any_conv) {
     if (kind >= 3)
       for (int r = r0; r < r1 && m0 + r < M; ++r)
@@ -836,7 +853,7 @@ __global__ __launch_bounds__(256, 1) void gemm_front_kernel(
     for (int q = 0; q < 4; ++q) {
       const int r = rb + q;
       const int t = m0 + r;
-      const bool emit = r < r1 && t < M;  // uniform within each 32-lane half
+      const bool emit = r < r1 && t < M;  // uniform within each lane group of a row
       const int back = t - sst[min(r, GBM - 1)];  // rows t-back .. t belong to t's sequence
       float y[8];
       float ss = 0.0f;
@@ -1261,17 +1278,32 @@ int replay_group_run(const sr_group_desc* d, const sr_gdn_layer_weights* weights
       const bool fuse = L.width <= 4 && !lconv0 && !conv_states &&
                         static_cast<size_t>(T) * d->hidden * 2 < (size_t{1} << 31);
       if (fuse) {
+        // A projection of at most 128 tiles (a small batch) runs as 256
+        // 128-column halves, so it spreads over twice as many CUs.  Larger
+        // ones stay whole tiles in one launch: a second launch for the
+        // halves of a partly filled last round waits for the first to drain,
+        // which measured slower than the one launch, whose last tiles start
+        // as CUs free up (96,829 tokens: 24.1 against 23.9 ms per group).
         const int n_m = (T + sr::FTM - 1) / sr::FTM, n_n = (N + sr::GBN - 1) / sr::GBN;
-        const dim3 grid((n_m * n_n + sr::kXcdG - 1) / sr::kXcdG * sr::kXcdG);
-        if (d->d == 128)
-          hipLaunchKernelGGL(sr::gemm_front_kernel<128>, grid, dim3(256), 0, s, xh, d->hidden, win,
-                             d->hidden, T, N, d->hidden, L, convw, sst, d->l2_eps, P, L.n_all(),
-                             qb, kb, vb);
-        else
-          hipLaunchKernelGGL(sr::gemm_front_kernel<64>, grid, dim3(256), 0, s, xh, d->hidden, win,
-                             d->hidden, T, N, d->hidden, L, convw, sst, d->l2_eps, P, L.n_all(),
-                             qb, kb, vb);
-        if (hipGetLastError() != hipSuccess) return SR_ELAUNCH;
+        const int tiles = n_m * n_n;
+        const int halves = 2 * tiles <= kGfx950Cus ? tiles : 0;
+        const int whole = tiles - halves;
+        auto front = [&](auto kern, int nblk, int q0, int nq) {
+          if (nq == 0) return hipSuccess;
+          hipLaunchKernelGGL(kern, dim3(nblk), dim3(256), 0, s, xh, d->hidden, win, d->hidden, T, N,
+                             d->hidden, L, convw, sst, d->l2_eps, P, L.n_all(), qb, kb, vb, q0, nq);
+          return hipGetLastError();
+        };
+        const int gw = (whole + sr::kXcdG - 1) / sr::kXcdG * sr::kXcdG;
+        hipError_t e1, e2;
+        if (d->d == 128) {
+          e1 = front(sr::gemm_front_kernel<128, 4>, gw, 0, whole);
+          e2 = front(sr::gemm_front_kernel<128, 2>, 2 * halves, whole, halves);
+        } else {
+          e1 = front(sr::gemm_front_kernel<64, 4>, gw, 0, whole);
+          e2 = front(sr::gemm_front_kernel<64, 2>, 2 * halves, whole, halves);
+        }
+        if (e1 != hipSuccess || e2 != hipSuccess) return SR_ELAUNCH;
         const size_t ng = static_cast<size_t>(T) * d->h_v;
         hipLaunchKernelGGL(sr::gates_kernel, dim3(static_cast<unsigned>((ng + 255) / 256)), dim3(256),
                            0, s, P, L.n_all(), L, T, la, be);
