@@ -547,7 +547,10 @@ __global__ __launch_bounds__(64) void gemm_block_kernel(const _Float16* __restri
   const uint32_t bo = static_cast<uint32_t>(
       (static_cast<size_t>(min(n0 + l % 32, N - 1)) * ldb + 8 * (l / 32)) * 2);
   const int ns = K / 16;  // k16 steps
-  constexpr int PF = 32;  // steps in flight
+  // PF steps in flight (2 PF loads outstanding, within the wait counter's
+  // range); the chunks of PF steps have no branch between the MFMAs, so
+  // each MFMA waits for its own operands only
+  constexpr int PF = 16;
   f16x8 ar[PF], br[PF];
   auto load = [&](int p, int step) {
     const int k0 = 16 * min(step, ns - 1);  // past the end: reload the last step (never used)
@@ -559,13 +562,22 @@ __global__ __launch_bounds__(64) void gemm_block_kernel(const _Float16* __restri
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-  for (int s0 = 0; s0 < ns; s0 += PF) {
+  const int nfull = ns / PF * PF;
+  for (int s0 = 0; s0 < nfull; s0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      if (s0 + p < ns) acc = mfma32x32x16(br[p], ar[p], acc);
+      acc = mfma32x32x16(br[p], ar[p], acc);
       load(p, s0 + p + PF);
+      // keep each refill next to its MFMA (left to itself the scheduler
+      // sinks all refills to the end of the chunk, and the chunk's last
+      // MFMA then waits for every load in flight)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // the last ns - nfull steps (K % (16 PF) != 0) sit in slots 0, 1, ...
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < ns - nfull) acc = mfma32x32x16(br[p], ar[p], acc);
   // lane l: row m0 + l%32; register group g: columns n0 + 8g + 4(l/32) .. +3
   const int m = m0 + l % 32;
   if (m >= M) return;
